@@ -1,0 +1,258 @@
+"""Benchmark: one paged decode step = new-token cache write + decode attention
+over a synthetic batch resident in HBM, on one MI355X.
+
+Prints ONE JSON line (last line of stdout).  ``value`` is the step's
+algorithmic bytes (K/V rows actually attended, Q, output, table entries,
+lengths, plus the cache write's reads and writes) per second of wall time
+over the timed steps.  ``roofline`` reports the decode kernel alone: its
+algorithmic bytes divided by its average duration from HIP events recorded
+on the stream it runs on.  ``cpu_baseline`` is the fp64 oracle on host cores
+over the same workload, measured before the GPU is touched.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import pathlib
+import sys
+import time
+
+import numpy as np
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+from synthetic import WORKLOADS, algorithmic_bytes, kv_token_count, make_case  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and KV tokens/sec"
+DEFAULT_ENTRY = {"llama2_7b": ("splitk", 256), "long_bs512": ("splitk", 512),
+                 "gqa_70b": ("splitk", 512), "shared_prefix": ("splitk", 256),
+                 "tiny": ("single", None)}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- CPU baseline
+_CASE = None
+
+
+def _worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_one(s):
+    import oracle
+    c = _CASE
+    o = oracle.decode(c.q[s:s + 1], c.k_pool, c.v_pool, c.block_tables[s:s + 1],
+                      c.context_lens[s:s + 1], c.scale, c.block_size, c.dtype)
+    return s, o
+
+
+def cpu_baseline(case, min_seconds: float) -> dict:
+    """Time the fp64 oracle over whole passes of the workload (all sequences,
+    all heads) with a fork pool, until at least ``min_seconds`` have passed."""
+    global _CASE
+    _CASE = case
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    workers = max(1, min(avail, 16))
+    B = case.workload.num_seqs
+    tokens = kv_token_count(case)
+    order = list(np.argsort(-case.context_lens.astype(np.int64)))   # longest first
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_worker_init) as pool:
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            res = pool.map(_oracle_one, order, chunksize=1)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or passes >= 1000:
+                break
+    assert len(res) == B
+    cpu_model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": passes * tokens / el, "unit": "KV tokens/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) over all {B} sequences x "
+                      f"{case.workload.num_heads} heads ({tokens} KV tokens per pass), "
+                      f"fp64 NumPy, fork pool of {workers} workers, {el:.1f} s wall",
+            "cpu_model": cpu_model, "os_cpu_count": os.cpu_count()}
+
+
+# ----------------------------------------------------------------- GPU run
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama2_7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--entry", default=None, choices=["single", "splitk"])
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, run torch copies of this many MiB "
+                         "(calibrates HBM byte counters under rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): paged decode shards by sequence or KV head with no exchange inside "
+              "attention, and this build measures the single-GPU kernel.", flush=True)
+        return 2
+
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return 0
+
+    w = WORKLOADS[args.workload]
+    entry, P = DEFAULT_ENTRY[w.name]
+    if args.entry:
+        entry = args.entry
+        P = args.partition or (w.partition_size or 256) if entry == "splitk" else None
+    elif args.partition:
+        P = args.partition
+    t = time.perf_counter()
+    case = make_case(w, seed=args.seed)
+    log(f"bench: generated {w.name} seed={case.seed} in {time.perf_counter() - t:.1f} s; "
+        f"sum L = {kv_token_count(case)}, pool blocks = {case.num_blocks}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, args.cpu_seconds)      # before any GPU call (fork)
+        log(f"bench: cpu baseline {cpu['value']:.4g} KV tokens/s on {cpu['cores']} workers")
+
+    import torch
+    import paged_kv_cache_438_amd as pa
+    if not pa.LIB_PATH.exists():
+        raise SystemExit("libpa.so is not built: run python __graft_entry__.py build")
+    dev = torch.device("cuda:0")
+
+    def d(a, dt=None):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    dt = case.dtype
+    q, kp, vp = d(case.q, dt), d(case.k_pool, dt), d(case.v_pool, dt)
+    kn, vn = d(case.k_new, dt), d(case.v_new, dt)
+    tb, ln = d(case.block_tables), d(case.context_lens)
+    out = torch.empty_like(q)
+    maxlen = int(case.context_lens.max())
+    scale = float(case.scale)
+    ws = None
+    if entry == "splitk":
+        need = pa.pa_decode_splitk_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, maxlen, P)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def decode():
+        if entry == "single":
+            pa.pa_decode(q, kp, vp, tb, ln, scale=scale, out=out)
+        else:
+            pa.pa_decode_splitk(q, kp, vp, tb, ln, partition_size=P, max_context_len=maxlen,
+                                scale=scale, out=out, workspace=ws)
+
+    def step():
+        pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
+        decode()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
+        evs[i][0].record()
+        decode()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    e = w.elem_bytes
+    dec_bytes = algorithmic_bytes(case)
+    cw_bytes = 4 * w.num_seqs * w.num_kv_heads * w.head_dim * e + 4 * 2 * w.num_seqs
+    step_bytes = dec_bytes + cw_bytes
+    ms_step = elapsed * 1e3 / K
+    value = step_bytes * K / elapsed / 1e9
+    tokens = kv_token_count(case)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    traffic = None
+    tf = ROOT / "profiles" / f"traffic_{w.name}_{entry}.json"
+    if tf.exists():
+        try:
+            rec = json.loads(tf.read_text())
+            import hashlib
+            src = (ROOT / "paged_kv_cache_438_amd" / "csrc" / "pa_kernels.hip").read_bytes()
+            if rec.get("kernel_source_sha256") == hashlib.sha256(src).hexdigest():
+                traffic = rec.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    kernel = "k_decode" if entry == "single" else "k_decode (partitions) + k_reduce"
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[dt],
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "seed": case.seed,
+                   "entry": "pa_decode" if entry == "single" else "pa_decode_splitk",
+                   "partition_size": P, "accumulate": "f32",
+                   "global_batch": w.num_seqs, "kv_tokens": tokens,
+                   "step": "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
+        "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": kernel,
+                     "avg_launch_us": round(dec_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": dec_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

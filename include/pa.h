@@ -1,0 +1,174 @@
+/*
+ * pa.h -- C ABI of libpa: paged KV-cache decode attention on AMD MI355X (gfx950).
+ *
+ * The data model follows the pages' description of paged KV caching:
+ *   - the KV cache is one pool of fixed-size blocks ("pages"), each holding the
+ *     keys (or values) of `block_size` consecutive tokens
+ *     ("IO-5 vLLM Paged Attention", section 3 "KV Cache Paging structure";
+ *      "Efficient Memory Management for LLM Serving with PagedAttention (vLLM)
+ *      paper summary", key feature 1 "KV cache blocking");
+ *   - each sequence owns a block table listing, in logical order, the physical
+ *     blocks that hold its tokens, so its memory need not be contiguous
+ *     ("IO-5 vLLM Paged Attention", section 2 "Paged Attention idea");
+ *   - decode attention is softmax(q K^T * scale) V, with K and V the
+ *     sequence's blocks concatenated in table order
+ *     ("IO-5 vLLM Paged Attention", section 4 "Attention computation").
+ *
+ * Layouts (all row-major, element type `dtype`):
+ *   q, out        [num_seqs][num_heads][head_dim]
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim]
+ *   k_pool,v_pool [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs]
+ * Token t of sequence s, KV head g, lives at
+ *   pool[block_tables[s][t / block_size]][g][t % block_size][:].
+ * Query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Ownership and execution: every pointer argument is a DEVICE pointer owned by
+ * the caller (except pa_check_inputs_host, which takes HOST pointers).  The
+ * library allocates nothing and keeps no pointer after a call returns.  Every
+ * call only enqueues work on `stream` (a hipStream_t; NULL = the null stream)
+ * and returns without synchronising.  Calls are thread-safe; the only global
+ * state is the calling thread's last-error string.
+ *
+ * Errors: the host-side scalar checks below run before anything is enqueued; a
+ * failing call returns a nonzero pa_status, enqueues nothing and records a
+ * message for pa_last_error().  Device data (lengths, table entries) are not
+ * read by the host.  If they break the contract, the kernels do not read or
+ * write outside the buffers: an out-of-range length or block id makes that
+ * sequence's output NaN (decode) or skips that sequence's write (cache write).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,          /* a required pointer is NULL */
+  PA_ERR_INVALID_ARG = 2,   /* a size or relation between sizes is invalid */
+  PA_ERR_UNSUPPORTED = 3,   /* head_dim, block_size or dtype not built */
+  PA_ERR_WORKSPACE = 4,     /* split-K workspace missing or too small */
+  PA_ERR_HIP = 5            /* the HIP runtime reported an error on launch */
+} pa_status;
+
+/* Supported shapes: head_dim in {64, 128}; block_size a power of two in
+ * [1, 1024]; num_heads a multiple of num_kv_heads; dtype one of pa_dtype. */
+
+/* Version of this ABI (PA_ABI_VERSION of the built library). */
+int pa_abi_version(void);
+
+/* Static text for a pa_status value. */
+const char* pa_status_str(int status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_cache_write -- store each sequence's newest token into its block.
+ *
+ * The pages have a sequence's K/V stored block by block through its table
+ * ("IO-5 vLLM Paged Attention", sections 2-3) and blocks handed out on demand
+ * ("Efficient Memory Management ... paper summary", key feature 4); the write
+ * of the token being decoded is not described there.  Reading used here:
+ * context_lens[s] already counts the new token, which is logical position
+ * L-1 with L = context_lens[s]; the caller has already placed a block in the
+ * table for that position.  For every sequence with L >= 1 and every KV head
+ * g the head_dim elements of k_new[s][g] and v_new[s][g] are copied, bit for
+ * bit, to row (L-1) % block_size of block block_tables[s][(L-1)/block_size]
+ * of k_pool and v_pool.  L = 0 writes nothing.  No other byte changes.
+ * Two sequences must not name the same slot (undefined which write wins).
+ *
+ * num_seqs == 0 is a no-op (pointers may then be NULL).
+ */
+int pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                   int max_blocks_per_seq, int num_blocks, int dtype, void* stream);
+
+/*
+ * pa_decode -- single-pass paged decode attention.
+ *
+ * out[s][h] = softmax(q[s][h] . K_s^T * scale) V_s, where K_s, V_s are the
+ * first L = context_lens[s] rows of KV head h / (num_heads/num_kv_heads) of
+ * the blocks block_tables[s][0 .. ceil(L/block_size)-1] concatenated in order
+ * ("IO-5 vLLM Paged Attention", section 4 "Attention computation"; block
+ * count as in "vLLM's efficiency secret: PagedAttention and dynamic memory
+ * management", section "Dynamic memory management").  Rows past L and table
+ * entries past ceil(L/block_size) are never read and may hold anything.
+ * Products and sums are accumulated in fp32; the result is rounded once to
+ * `dtype` (nearest-even).  L = 0 gives a zero row.  `scale` is usually
+ * 1/sqrt(head_dim).  `out` must not overlap any input.
+ *
+ * One launch; no workspace.  Device contract: 0 <= L <= max_blocks_per_seq *
+ * block_size and 0 <= block_tables[s][i] < num_blocks for i < ceil(L/bs);
+ * a sequence that breaks it gets a NaN output row.
+ */
+int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* context_lens,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+              int block_size, int max_blocks_per_seq, int num_blocks,
+              float scale, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace pa_decode_splitk needs for these sizes: fp32
+ * partial results for num_seqs * num_heads * ceil(max_context_len /
+ * partition_size) partitions, each head_dim accumulators plus a running
+ * maximum and sum, rounded up to 256 bytes.  Returns 0 for invalid sizes.
+ */
+size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                        int max_context_len, int partition_size);
+
+/*
+ * pa_decode_splitk -- the same result as pa_decode, computed in two launches
+ * for long contexts: each sequence's tokens are cut into partitions of
+ * `partition_size` tokens (a positive multiple of 16); the first launch
+ * computes, per (sequence, head, partition), the partition's maximum score m,
+ * sum of exp(score - m) and unnormalised weighted value sum into `workspace`;
+ * the second merges the partitions of each (sequence, head) in fixed order,
+ * rescaling each by exp(m_p - max_p m_p), and writes `out`.  Sequences with a
+ * single partition are written directly by the first launch.
+ *
+ * max_context_len is a host-known bound on every context_lens[s] (no device
+ * to host copy is made); it must not exceed max_blocks_per_seq * block_size.
+ * A sequence longer than it gets a NaN output row.  `workspace` must hold
+ * pa_decode_splitk_workspace_bytes(...) bytes, 16-byte aligned; its contents
+ * on entry do not matter and are undefined on exit.
+ */
+int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                     int block_size, int max_blocks_per_seq, int num_blocks,
+                     float scale, int dtype, int partition_size, int max_context_len,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_check_inputs_host -- validate HOST copies of the device data against the
+ * contract above: 0 <= L <= max_blocks_per_seq * block_size, every table entry
+ * in use in [0, num_blocks), and, if check_write_targets is nonzero, that no
+ * two sequences' newest tokens map to the same (block, row).  Returns PA_OK or
+ * PA_ERR_INVALID_ARG; on failure *bad_seq (if not NULL) receives the first
+ * offending sequence and pa_last_error() says what is wrong.  Pure host code.
+ */
+int pa_check_inputs_host(const int32_t* block_tables, const int32_t* context_lens,
+                         int num_seqs, int block_size, int max_blocks_per_seq,
+                         int num_blocks, int check_write_targets, int* bad_seq);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,214 @@
+"""ctypes binding of libpa (include/pa.h).
+
+Argument marshalling only: torch tensors supply device memory and the stream;
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if libpa.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import re
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = pathlib.Path(__file__).resolve().parent / "libpa.so"
+HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "pa.h"
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+_DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+_c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+_SIGNATURES = {
+    "pa_abi_version": (_c_int, []),
+    "pa_status_str": (ctypes.c_char_p, [_c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_cache_write": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_void_p]),
+    "pa_decode": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p]),
+    "pa_decode_splitk_workspace_bytes": (_c_size_t, [_c_int] * 5),
+    "pa_decode_splitk": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
+                         [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p]),
+    "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
+                             [ctypes.POINTER(_c_int)]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func} failed: {status_str(status)} ({status}): {detail}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950); there is no fallback path")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/pa.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def status_str(status: int) -> str:
+    return load().pa_status_str(status).decode()
+
+
+def last_error() -> str:
+    return load().pa_last_error().decode()
+
+
+def abi_version() -> int:
+    return load().pa_abi_version()
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise PaError(status, func, last_error())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _pool_shape(k_pool, v_pool) -> Tuple[int, int, int, int]:
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool must both be [num_blocks][num_kv_heads][block_size][head_dim]")
+    return tuple(k_pool.shape)
+
+
+def _meta(block_tables, context_lens, B):
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    if context_lens.shape != (B,):
+        raise ValueError("context_lens must be [num_seqs]")
+    return block_tables.shape[1]
+
+
+def pa_cache_write(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tensor,
+                   v_new: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   stream=None) -> None:
+    """Store each sequence's newest token (position context_lens[s]-1) into its
+    block slot, in place.  See pa_cache_write in include/pa.h."""
+    for n, t in (("k_pool", k_pool), ("v_pool", v_pool), ("k_new", k_new), ("v_new", v_new)):
+        _dev(t, n)
+    NB, Hkv, bs, d = _pool_shape(k_pool, v_pool)
+    if k_new.dim() != 3 or k_new.shape[1:] != (Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if not (k_pool.dtype == v_pool.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("pools and new rows must share one dtype")
+    B = k_new.shape[0]
+    MB = _meta(block_tables, context_lens, B)
+    st = load().pa_cache_write(k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(),
+                               v_new.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+                               B, Hkv, d, bs, MB, NB, _DTYPES.get(k_pool.dtype, -1),
+                               _stream(k_pool.device, stream))
+    _check(st, "pa_cache_write")
+
+
+def _decode_args(q, k_pool, v_pool, block_tables, context_lens, scale, out):
+    for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(t, n)
+    NB, Hkv, bs, d = _pool_shape(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != d:
+        raise ValueError("q must be [num_seqs][num_heads][head_dim]")
+    if not (q.dtype == k_pool.dtype == v_pool.dtype):
+        raise TypeError("q and the pools must share one dtype")
+    B, Hq, _ = q.shape
+    MB = _meta(block_tables, context_lens, B)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    return out, (B, Hq, Hkv, d, bs, MB, NB), float(scale)
+
+
+def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+              block_tables: torch.Tensor, context_lens: torch.Tensor,
+              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Single-pass paged decode attention; returns ``out`` [num_seqs][num_heads][head_dim]."""
+    out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
+                                                           context_lens, scale, out)
+    st = load().pa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                          block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, d, bs,
+                          MB, NB, scale, _DTYPES.get(q.dtype, -1), _stream(q.device, stream))
+    _check(st, "pa_decode")
+    return out
+
+
+def pa_decode_splitk_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
+                                     max_context_len: int, partition_size: int) -> int:
+    return int(load().pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                       max_context_len, partition_size))
+
+
+def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                     block_tables: torch.Tensor, context_lens: torch.Tensor,
+                     partition_size: int, max_context_len: int,
+                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Split-K paged decode attention (partition pass + reduce pass)."""
+    out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
+                                                           context_lens, scale, out)
+    need = pa_decode_splitk_workspace_bytes(B, Hq, d, max_context_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pa_decode_splitk(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(),
+                                 v_pool.data_ptr(), block_tables.data_ptr(),
+                                 context_lens.data_ptr(), B, Hq, Hkv, d, bs, MB, NB, scale,
+                                 _DTYPES.get(q.dtype, -1), int(partition_size),
+                                 int(max_context_len), workspace.data_ptr(), ws_bytes,
+                                 _stream(q.device, stream))
+    _check(st, "pa_decode_splitk")
+    return out
+
+
+def pa_check_inputs_host(block_tables, context_lens, block_size: int, num_blocks: int,
+                         check_write_targets: bool = False) -> Tuple[bool, int, str]:
+    """Validate host copies of the tables and lengths.  Returns
+    (ok, first bad sequence or -1, message)."""
+    import numpy as np
+    tb = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    ln = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if tb.ndim != 2 or ln.shape != (tb.shape[0],):
+        raise ValueError("block_tables must be [B][MB] and context_lens [B]")
+    bad = _c_int(-1)
+    st = load().pa_check_inputs_host(tb.ctypes.data, ln.ctypes.data, tb.shape[0], block_size,
+                                     tb.shape[1], num_blocks, int(bool(check_write_targets)),
+                                     ctypes.byref(bad))
+    return st == 0, bad.value, last_error()

@@ -1,0 +1,54 @@
+"""Build libpa.so (HIP kernels + C ABI) in-tree with hipcc for gfx950."""
+from __future__ import annotations
+
+import os
+import pathlib
+import shutil
+import subprocess
+import sys
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+LIB = PKG / "libpa.so"
+SOURCES = [CSRC / "pa_api.cpp", CSRC / "pa_kernels.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def compile_flags() -> list:
+    return [
+        "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+        # keep packed fp32 arithmetic out of the generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        f"-I{ROOT / 'include'}", f"-I{CSRC}",
+    ]
+
+
+def build(verbose: bool = False) -> pathlib.Path:
+    """Compile every source into libpa.so (always recompiles)."""
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [hipcc()] + compile_flags() + [str(s) for s in SOURCES] + ["-o", str(tmp)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd=str(PKG), capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    noise = [ln for ln in (res.stdout + res.stderr).splitlines()
+             if ln.strip() and "packed-fp32-ops" not in ln]
+    if verbose and noise:
+        print("\n".join(noise), flush=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,264 @@
+// C ABI of libpa (declared in include/pa.h): host-side argument checks,
+// then one or two kernel launches on the caller's stream.  No allocation,
+// no synchronisation, no device-to-host copy.
+#include "pa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <unordered_set>
+
+#include "pa_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                 int max_blocks_per_seq, int num_blocks, int dtype) {
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", num_kv_heads);
+  if (max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", num_blocks);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!is_pow2(block_size) || block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (power of two in [1,1024])", block_size);
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if ((long long)max_blocks_per_seq * block_size > 0x3fffffffLL)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
+  return PA_OK;
+}
+
+int check_decode(const void* out, const void* q, const void* k_pool, const void* v_pool,
+                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                 int num_heads, int num_kv_heads, int head_dim, int block_size,
+                 int max_blocks_per_seq, int num_blocks, float scale, int dtype) {
+  int st = check_common(num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, dtype);
+  if (st) return st;
+  if (num_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_heads must be > 0 (got %d)", num_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+                num_kv_heads);
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(PA_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
+  if (!aligned16(out))
+    return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  return PA_OK;
+}
+
+pa::DecodeParams make_params(void* out, const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int num_blocks,
+                             float scale, int dtype) {
+  pa::DecodeParams p;
+  p.out = out;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.workspace = nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.dtype = dtype;
+  p.partition_size = 0;
+  p.max_partitions = 1;
+  return p;
+}
+
+int finish_launch(hipError_t e) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                   int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                   int num_blocks, int dtype, void* stream) {
+  int st = check_common(num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                        num_blocks, dtype);
+  if (st) return st;
+  if (num_seqs == 0) return ok();
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_INVALID_ARG, "pools and new rows must be 16-byte aligned");
+  pa::CacheWriteParams p;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.dtype = dtype;
+  return finish_launch(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int max_blocks_per_seq, int num_blocks, float scale, int dtype, void* stream) {
+  int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                        dtype);
+  if (st) return st;
+  if (num_seqs == 0) return ok();
+  pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                                   num_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, num_blocks, scale, dtype);
+  // One partition spanning the longest sequence the tables can describe.
+  p.partition_size = (int)(ceil_div64((int64_t)max_blocks_per_seq * block_size, 16) * 16);
+  p.max_partitions = 1;
+  return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                        int max_context_len, int partition_size) {
+  if (num_seqs < 0 || num_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
+      max_context_len < 0 || partition_size <= 0 || partition_size % 16 != 0)
+    return 0;
+  const int parts = (int)ceil_div64(max_context_len, partition_size);
+  const size_t bytes = pa::splitk_partial_bytes(num_seqs, num_heads, head_dim, parts > 0 ? parts : 1);
+  return (bytes + 255) / 256 * 256;
+}
+
+int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                     int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                     int partition_size, int max_context_len, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                        dtype);
+  if (st) return st;
+  if (partition_size <= 0 || partition_size % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be a positive multiple of 16 (got %d)",
+                partition_size);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARG,
+                "max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (num_seqs == 0) return ok();
+  const size_t need = pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                       max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                                   num_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, num_blocks, scale, dtype);
+  const int parts = (int)ceil_div64(max_context_len, partition_size);
+  p.partition_size = partition_size;
+  p.max_partitions = parts > 0 ? parts : 1;
+  p.workspace = static_cast<float*>(workspace);
+  return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int pa_check_inputs_host(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                         int block_size, int max_blocks_per_seq, int num_blocks,
+                         int check_write_targets, int* bad_seq) {
+  if (bad_seq) *bad_seq = -1;
+  if (num_seqs < 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "invalid sizes");
+  if (num_seqs == 0) return ok();
+  if (!block_tables || !context_lens) return fail(PA_ERR_NULL, "a required pointer is NULL");
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  std::unordered_set<int64_t> slots;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int64_t L = context_lens[s];
+    if (L < 0 || L > cap) {
+      if (bad_seq) *bad_seq = s;
+      return fail(PA_ERR_INVALID_ARG, "sequence %d: length %lld outside [0, %lld]", s,
+                  (long long)L, (long long)cap);
+    }
+    const int64_t nb = ceil_div64(L, block_size);
+    const int32_t* row = block_tables + (size_t)s * max_blocks_per_seq;
+    for (int64_t i = 0; i < nb; ++i) {
+      if (row[i] < 0 || row[i] >= num_blocks) {
+        if (bad_seq) *bad_seq = s;
+        return fail(PA_ERR_INVALID_ARG, "sequence %d: block table entry %lld = %d outside [0, %d)",
+                    s, (long long)i, row[i], num_blocks);
+      }
+    }
+    if (check_write_targets && L >= 1) {
+      const int64_t pos = L - 1;
+      const int64_t slot = (int64_t)row[pos / block_size] * block_size + pos % block_size;
+      if (!slots.insert(slot).second) {
+        if (bad_seq) *bad_seq = s;
+        return fail(PA_ERR_INVALID_ARG,
+                    "sequence %d: new-token slot (block %d, row %lld) already written by another "
+                    "sequence", s, row[pos / block_size], (long long)(pos % block_size));
+      }
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal interface between the C ABI (pa_api.cpp) and the HIP kernels
+// (pa_kernels.hip).  Not installed; callers use include/pa.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* workspace;        // split-K partials; nullptr for a single pass
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int max_blocks_per_seq;
+  int num_blocks;
+  float scale;
+  int dtype;
+  int partition_size;      // tokens per partition (multiple of 16)
+  int max_partitions;      // partitions per sequence covered by the grid
+};
+
+struct CacheWriteParams {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int max_blocks_per_seq;
+  int num_blocks;
+  int dtype;
+};
+
+// Byte size of the split-K partials for these sizes (no rounding).
+size_t splitk_partial_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions);
+
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
+// Single pass when p.workspace == nullptr (then p.max_partitions must be 1).
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace pa

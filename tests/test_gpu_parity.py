@@ -1,0 +1,313 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test here needs an MI355X and the built libpa.so.  Floating-point
+outputs must stay within the max-abs bounds 1e-5 (fp32), 2e-3 (fp16),
+1e-2 (bf16); cache-write placement and block-table indexing must be
+bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_438_amd as pa
+from synthetic import (GQA70B, LLAMA7B, LONG_BS512, SHARED_PREFIX, TINY, WORKLOADS, Workload,
+                       make_case, small_variant, to_storage)
+from tests import pins
+from tests.gpu_util import TOL, DevCase, host_bits, host_f64, note
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [small_variant(w) for w in WORKLOADS.values()]
+ENTRIES = [("single", None), ("splitk", 16), ("splitk", 64), ("splitk", 512)]
+
+
+def _oracle(c, kp=None, vp=None, tb=None, pairs=None):
+    return oracle.decode(c.q, c.k_pool if kp is None else kp, c.v_pool if vp is None else vp,
+                         c.block_tables if tb is None else tb, c.context_lens, c.scale,
+                         c.block_size, c.dtype, pairs=pairs)
+
+
+def _check_close(got, ref, dtype, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    note(f"  {what}: max|err| = {err:.3e} (bound {TOL[dtype]:.0e})")
+    assert err <= TOL[dtype], f"{what}: max abs error {err} > {TOL[dtype]}"
+
+
+# ------------------------------------------------------------------ cache write
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_cache_write_bit_exact(w):
+    c = make_case(w)
+    note(f"cache_write: {w.name} seed={c.seed} B={w.num_seqs} dtype={w.dtype}")
+    kp0, vp0 = c.pools_with_new_slots_poisoned()
+    d = DevCase(c, k_pool=kp0, v_pool=vp0)
+    d.cache_write()
+    torch.cuda.synchronize()
+    kp_exp, vp_exp = oracle.cache_write(kp0, vp0, c.k_new, c.v_new, c.block_tables,
+                                        c.context_lens, c.block_size)
+    assert host_bits(d.k_pool).tobytes() == kp_exp.tobytes()
+    assert host_bits(d.v_pool).tobytes() == vp_exp.tobytes()
+    # and the written pool is the fully populated one the generator built
+    assert kp_exp.tobytes() == c.k_pool.tobytes()
+
+
+# ------------------------------------------------------------------ small parity
+@pytest.mark.parametrize("entry,P", ENTRIES, ids=lambda x: str(x))
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_decode_parity_small(w, entry, P):
+    c = make_case(w)
+    note(f"decode: {w.name} seed={c.seed} entry={entry} P={P} lens={c.context_lens.tolist()}")
+    d = DevCase(c)
+    out = d.decode(entry, P)
+    torch.cuda.synchronize()
+    _check_close(host_f64(out), _oracle(c), w.dtype, f"{w.name}/{entry}/{P}")
+
+
+def test_end_to_end_tiny_write_then_decode():
+    """Pre-filled pool minus the newest token, write it, then decode."""
+    c = make_case(TINY)
+    kp0, vp0 = c.pools_with_new_slots_poisoned()
+    d = DevCase(c, k_pool=kp0, v_pool=vp0)
+    d.cache_write()
+    for entry, P in ENTRIES:
+        out = d.decode(entry, P)
+        torch.cuda.synchronize()
+        _check_close(host_f64(out), _oracle(c), "f32", f"tiny/{entry}/{P}")
+
+
+# ------------------------------------------------------------------ edge lengths
+EDGE = [
+    # (name, lens, Hq, Hkv, d, bs, dtype, partition)
+    ("bs16_f16_mha", (0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 513), 2, 2, 128, 16, "f16", 64),
+    ("bs1_bf16_g2", (0, 1, 2, 3, 15, 16, 17, 33, 47, 48, 49), 4, 2, 64, 1, "bf16", 16),
+    ("bs2_f32_g4", (1, 2, 3, 31, 32, 33, 100), 8, 2, 128, 2, "f32", 32),
+    ("bs4_f16_g3", (0, 5, 16, 17, 64, 90), 6, 2, 64, 4, "f16", 48),
+    ("bs8_bf16_g8", (1, 7, 8, 9, 31, 32, 33, 200), 16, 2, 128, 8, "bf16", 64),
+    ("bs512_bf16", (1, 511, 512, 513, 1023, 1024, 1025, 1600), 2, 2, 128, 512, "bf16", 512),
+    ("bs1024_f16_p512", (1, 511, 512, 513, 1024, 1025, 2047, 2048), 2, 1, 64, 1024, "f16", 512),
+    ("bs64_f32_d64", (0, 63, 64, 65, 128, 129, 300), 2, 1, 64, 64, "f32", 128),
+]
+
+
+def edge_workload(name, lens, Hq, Hkv, d, bs, dtype, P, seed=17):
+    mb = max(1, max(-(-L // bs) for L in lens))
+    return Workload(name=name, num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                    block_size=bs, dtype=dtype, seed=seed, length_kind="fixed",
+                    lengths=tuple(lens), max_blocks_per_seq=mb + 1, partition_size=P)
+
+
+@pytest.mark.parametrize("spec", EDGE, ids=lambda s: s[0])
+def test_decode_edge_lengths(spec):
+    w = edge_workload(*spec)
+    c = make_case(w)
+    ref = _oracle(c)
+    d = DevCase(c)
+    for entry, P in (("single", None), ("splitk", w.partition_size), ("splitk", 16)):
+        note(f"edge: {w.name} entry={entry} P={P} lens={list(w.lengths)}")
+        out = d.decode(entry, P)
+        torch.cuda.synchronize()
+        got = host_f64(out)
+        _check_close(got, ref, w.dtype, f"{w.name}/{entry}/{P}")
+        for s, L in enumerate(w.lengths):
+            if L == 0:
+                assert np.all(got[s] == 0.0), "empty sequence must give zeros"
+
+
+# ------------------------------------------------------------------ bit-exact indexing
+def _needle_case(w, seed):
+    """Every query is 32*e_0; key component 0 is 0 everywhere except one
+    seeded needle token per sequence, where it is 72.  The needle's score
+    exceeds all others by > 200 (natural log), so its weight is exactly 1
+    and every other weight exactly 0 in fp32: the output must equal the
+    needle's value row bit for bit."""
+    c = make_case(w, seed=seed)
+    rng = np.random.default_rng(seed + 99)
+    st = lambda x: to_storage(np.array([x], dtype=np.float32), w.dtype)[0]
+    c.q[...] = st(0.0)
+    c.q[:, :, 0] = st(32.0)
+    c.k_pool[:, :, :, 0] = st(0.0)
+    needles = []
+    bs = w.block_size
+    for s, L in enumerate(c.context_lens):
+        L = int(L)
+        if L == 0:
+            needles.append(-1)
+            continue
+        choices = [0, L - 1, min(bs - 1, L - 1), min(bs, L - 1), int(rng.integers(L))]
+        pos = int(choices[s % len(choices)])
+        c.k_pool[c.block_tables[s, pos // bs], :, pos % bs, 0] = st(72.0)
+        needles.append(pos)
+    return c, needles
+
+
+@pytest.mark.parametrize("spec", [EDGE[0], EDGE[1], EDGE[2], EDGE[4], EDGE[5], EDGE[6]],
+                         ids=lambda s: s[0])
+def test_needle_bit_exact(spec):
+    w = edge_workload(*spec)
+    c, needles = _needle_case(w, seed=5)
+    d = DevCase(c)
+    G = w.num_heads // w.num_kv_heads
+    for entry, P in (("single", None), ("splitk", w.partition_size), ("splitk", 16)):
+        note(f"needle: {w.name} entry={entry} P={P} needles={needles}")
+        got = host_bits(d.decode(entry, P))
+        for s, pos in enumerate(needles):
+            if pos < 0:
+                continue
+            blk, row = c.block_tables[s, pos // w.block_size], pos % w.block_size
+            for h in range(w.num_heads):
+                exp = c.v_pool[blk, h // G, row]
+                assert got[s, h].tobytes() == exp.tobytes(), (s, h, pos, entry, P)
+
+
+@pytest.mark.parametrize("w", [TINY, small_variant(LONG_BS512), small_variant(GQA70B),
+                               small_variant(LLAMA7B)], ids=lambda w: w.name)
+def test_permutation_invariance_bitwise(w):
+    c = make_case(w)
+    kp, vp, tb = pins.relabel_blocks(c, np.random.default_rng(3))
+    a, b = DevCase(c), DevCase(c, k_pool=kp, v_pool=vp, tables=tb)
+    for entry, P in (("single", None), ("splitk", 32)):
+        note(f"permutation: {w.name} entry={entry}")
+        assert host_bits(a.decode(entry, P)).tobytes() == host_bits(b.decode(entry, P)).tobytes()
+
+
+def test_shared_prefix_equals_duplicated_bitwise():
+    c = make_case(small_variant(SHARED_PREFIX))
+    kp, vp, tb = pins.unshare_prefix(c)
+    a, b = DevCase(c), DevCase(c, k_pool=kp, v_pool=vp, tables=tb)
+    for entry, P in (("single", None), ("splitk", 32)):
+        note(f"shared-vs-duplicated: entry={entry}")
+        assert host_bits(a.decode(entry, P)).tobytes() == host_bits(b.decode(entry, P)).tobytes()
+
+
+def test_rerun_bitwise_deterministic():
+    c = make_case(small_variant(GQA70B))
+    d = DevCase(c)
+    for entry, P in (("single", None), ("splitk", 64)):
+        x = host_bits(d.decode(entry, P)).tobytes()
+        y = host_bits(d.decode(entry, P)).tobytes()
+        assert x == y
+
+
+# ------------------------------------------------------------------ contract handling
+def test_contract_violations_give_nan_not_faults():
+    """Lengths or block ids outside the contract: the kernels read nothing
+    out of bounds and flag the sequence with NaN; other sequences are exact."""
+    w = small_variant(LLAMA7B)
+    c = make_case(w)
+    ref = _oracle(c)
+    tb = c.block_tables.copy()
+    lens = c.context_lens.copy()
+    tb[1, 0] = c.num_blocks + 7                       # block id out of range
+    tb[2, 0] = -5
+    lens[3] = w.max_blocks_per_seq * w.block_size + 1  # longer than the table allows
+    d = DevCase(c, tables=tb)
+    d.lens = torch.from_numpy(lens).cuda()
+    for entry, P in (("single", None), ("splitk", 32)):
+        got = host_f64(d.decode(entry, P) if entry == "single" else pa.pa_decode_splitk(
+            d.q, d.k_pool, d.v_pool, d.tables, d.lens, partition_size=P,
+            max_context_len=w.max_blocks_per_seq * w.block_size, scale=float(c.scale)))
+        torch.cuda.synchronize()
+        for s in (1, 2, 3):
+            assert np.all(np.isnan(got[s])), (entry, s)
+        ok = [0, 4, 5]
+        assert np.max(np.abs(got[ok] - ref[ok])) <= TOL[w.dtype]
+    # max_context_len below a real length: that sequence is flagged
+    d2 = DevCase(c)
+    short = int(np.sort(c.context_lens)[-2])
+    got = host_f64(pa.pa_decode_splitk(d2.q, d2.k_pool, d2.v_pool, d2.tables, d2.lens,
+                                       partition_size=32, max_context_len=short,
+                                       scale=float(c.scale)))
+    for s, L in enumerate(c.context_lens):
+        if -(-int(L) // 32) > -(-short // 32):
+            assert np.all(np.isnan(got[s]))
+        else:
+            assert np.max(np.abs(got[s] - ref[s])) <= TOL[w.dtype]
+
+
+def test_cache_write_skips_out_of_contract_sequences():
+    c = make_case(TINY)
+    kp0, vp0 = c.pools_with_new_slots_poisoned()
+    tb = c.block_tables.copy()
+    tb[3, 2] = 99                                      # seq 3's newest token: bad block id
+    d = DevCase(c, k_pool=kp0, v_pool=vp0, tables=tb)
+    d.cache_write()
+    torch.cuda.synchronize()
+    kp_exp, _ = oracle.cache_write(kp0, vp0, c.k_new[:3], c.v_new[:3], c.block_tables[:3],
+                                   c.context_lens[:3], c.block_size)
+    assert host_bits(d.k_pool).tobytes() == kp_exp.tobytes()
+
+
+def test_api_errors_on_device():
+    c = make_case(TINY)
+    d = DevCase(c)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_splitk(d.q, d.k_pool, d.v_pool, d.tables, d.lens, partition_size=24,
+                            max_context_len=33)
+    assert e.value.status == 2
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_splitk(d.q, d.k_pool, d.v_pool, d.tables, d.lens, partition_size=16,
+                            max_context_len=33, workspace=torch.empty(64, dtype=torch.uint8,
+                                                                      device="cuda"))
+    assert e.value.status == 4
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_decode_splitk(d.q, d.k_pool, d.v_pool, d.tables, d.lens, partition_size=16,
+                            max_context_len=49)       # > max_blocks_per_seq * block_size
+    assert e.value.status == 2
+
+
+# ------------------------------------------------------------------ full-size, sampled
+FULL = {
+    "llama2_7b": (LLAMA7B, [("single", None), ("splitk", 256)]),
+    "long_bs512": (LONG_BS512, [("splitk", 512)]),
+    "gqa_70b": (GQA70B, [("single", None), ("splitk", 512)]),
+    "shared_prefix": (SHARED_PREFIX, [("single", None), ("splitk", 256)]),
+}
+_full_cache = {}
+
+
+def _full_case(name):
+    if name not in _full_cache:
+        _full_cache.clear()
+        w = FULL[name][0]
+        note(f"generating full-size workload {name} (seed {w.seed})")
+        _full_cache[name] = make_case(w)
+    return _full_cache[name]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(name):
+    w, entries = FULL[name]
+    c = _full_case(name)
+    rng = np.random.default_rng(42)
+    B, Hq = w.num_seqs, w.num_heads
+    order = np.argsort(c.context_lens)
+    seqs = sorted(set([int(order[0]), int(order[-1])] + rng.integers(0, B, 14).tolist()))
+    pairs = [(s, int(h)) for s in seqs for h in rng.choice(Hq, size=min(Hq, 3), replace=False)]
+    ref = _oracle(c, pairs=pairs)
+    d = DevCase(c)
+    if w.cache_write:
+        d.cache_write()         # rewrites each newest token with its own bytes
+    for entry, P in entries:
+        note(f"full: {name} entry={entry} P={P} sampled pairs={len(pairs)}")
+        got = host_f64(d.decode(entry, P))
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(got)), "non-finite output at full size"
+        idx = tuple(np.array(pairs).T)
+        _check_close(got[idx], ref[idx], w.dtype, f"full/{name}/{entry}/{P}")
+    del d
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_full_size_shared_prefix_cache_write_bit_exact():
+    c = _full_case("shared_prefix")
+    kp0, vp0 = c.pools_with_new_slots_poisoned()
+    d = DevCase(c, k_pool=kp0, v_pool=vp0)
+    d.cache_write()
+    torch.cuda.synchronize()
+    assert host_bits(d.k_pool).tobytes() == c.k_pool.tobytes()
+    assert host_bits(d.v_pool).tobytes() == c.v_pool.tobytes()
