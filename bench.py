@@ -28,8 +28,8 @@ from synthetic import WORKLOADS, algorithmic_bytes, kv_token_count, make_case  #
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and KV tokens/sec"
-DEFAULT_ENTRY = {"llama2_7b": ("splitk", 256), "long_bs512": ("splitk", 512),
-                 "gqa_70b": ("splitk", 512), "shared_prefix": ("splitk", 256),
+DEFAULT_ENTRY = {"llama2_7b": ("single", None), "long_bs512": ("splitk", 512),
+                 "gqa_70b": ("splitk", 512), "shared_prefix": ("single", None),
                  "tiny": ("single", None)}
 
 
@@ -173,12 +173,14 @@ def main() -> int:
         need = pa.pa_decode_splitk_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, maxlen, P)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
+    shared = case.shared_groups is not None      # tables alias a group's prompt blocks
+
     def decode():
         if entry == "single":
-            pa.pa_decode(q, kp, vp, tb, ln, scale=scale, out=out)
+            pa.pa_decode(q, kp, vp, tb, ln, scale=scale, out=out, shared_kv=shared)
         else:
             pa.pa_decode_splitk(q, kp, vp, tb, ln, partition_size=P, max_context_len=maxlen,
-                                scale=scale, out=out, workspace=ws)
+                                scale=scale, out=out, workspace=ws, shared_kv=shared)
 
     def step():
         pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
@@ -238,7 +240,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "seed": case.seed,
                    "entry": "pa_decode" if entry == "single" else "pa_decode_splitk",
-                   "partition_size": P, "accumulate": "f32",
+                   "partition_size": P, "accumulate": "f32", "shared_kv_flag": shared,
                    "global_batch": w.num_seqs, "kv_tokens": tokens,
                    "step": "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
         "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

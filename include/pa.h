@@ -65,6 +65,16 @@ typedef enum {
   PA_ERR_HIP = 5            /* the HIP runtime reported an error on launch */
 } pa_status;
 
+/* Decode flag bits.
+ * PA_FLAG_SHARED_KV: some blocks are named by more than one sequence's table
+ *   in this call (for example a prompt shared by parallel samples, block-level
+ *   sharing as in "Efficient Memory Management ... paper summary", key feature
+ *   2).  K/V loads then go through the caches normally so that later readers
+ *   of a shared block can hit.  Without it every K/V load carries the
+ *   non-temporal hint: each block is read once per call and would only
+ *   displace other cache lines.  The flag changes speed, never results. */
+#define PA_FLAG_SHARED_KV 1
+
 /* Supported shapes: head_dim in {64, 128}; block_size a power of two in
  * [1, 1024]; num_heads a multiple of num_kv_heads; dtype one of pa_dtype. */
 
@@ -113,6 +123,8 @@ int pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_
  * `dtype` (nearest-even).  L = 0 gives a zero row.  `scale` is usually
  * 1/sqrt(head_dim).  `out` must not overlap any input.
  *
+ * `flags` is 0 or PA_FLAG_SHARED_KV; other bits are rejected.
+ *
  * One launch; no workspace.  Device contract: 0 <= L <= max_blocks_per_seq *
  * block_size and 0 <= block_tables[s][i] < num_blocks for i < ceil(L/bs);
  * a sequence that breaks it gets a NaN output row.
@@ -121,7 +133,7 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* context_lens,
               int num_seqs, int num_heads, int num_kv_heads, int head_dim,
               int block_size, int max_blocks_per_seq, int num_blocks,
-              float scale, int dtype, void* stream);
+              float scale, int dtype, int flags, void* stream);
 
 /*
  * Bytes of device workspace pa_decode_splitk needs for these sizes: fp32
@@ -153,7 +165,7 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
                      int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                      int block_size, int max_blocks_per_seq, int num_blocks,
                      float scale, int dtype, int partition_size, int max_context_len,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     void* workspace, size_t workspace_bytes, int flags, void* stream);
 
 /*
  * pa_check_inputs_host -- validate HOST copies of the device data against the

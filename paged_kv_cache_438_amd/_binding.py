@@ -17,6 +17,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().parent / "libpa.so"
 HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "pa.h"
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_FLAG_SHARED_KV = 1
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 _c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
@@ -25,10 +26,11 @@ _SIGNATURES = {
     "pa_status_str": (ctypes.c_char_p, [_c_int]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_cache_write": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_void_p]),
-    "pa_decode": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_void_p]),
+    "pa_decode": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_int, _c_void_p]),
     "pa_decode_splitk_workspace_bytes": (_c_size_t, [_c_int] * 5),
     "pa_decode_splitk": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
-                         [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p]),
+                         [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
+                          _c_void_p]),
     "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
                              [ctypes.POINTER(_c_int)]),
 }
@@ -158,13 +160,16 @@ def _decode_args(q, k_pool, v_pool, block_tables, context_lens, scale, out):
 def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor,
               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-              stream=None) -> torch.Tensor:
-    """Single-pass paged decode attention; returns ``out`` [num_seqs][num_heads][head_dim]."""
+              shared_kv: bool = False, stream=None) -> torch.Tensor:
+    """Single-pass paged decode attention; returns ``out`` [num_seqs][num_heads][head_dim].
+    ``shared_kv``: some blocks appear in several sequences' tables (keeps K/V
+    loads cached instead of streaming); results are identical either way."""
     out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
                                                            context_lens, scale, out)
     st = load().pa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                           block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, d, bs,
-                          MB, NB, scale, _DTYPES.get(q.dtype, -1), _stream(q.device, stream))
+                          MB, NB, scale, _DTYPES.get(q.dtype, -1),
+                          PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
     _check(st, "pa_decode")
     return out
 
@@ -179,7 +184,8 @@ def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                      block_tables: torch.Tensor, context_lens: torch.Tensor,
                      partition_size: int, max_context_len: int,
                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                     workspace: Optional[torch.Tensor] = None, shared_kv: bool = False,
+                     stream=None) -> torch.Tensor:
     """Split-K paged decode attention (partition pass + reduce pass)."""
     out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
                                                            context_lens, scale, out)
@@ -193,7 +199,7 @@ def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                                  context_lens.data_ptr(), B, Hq, Hkv, d, bs, MB, NB, scale,
                                  _DTYPES.get(q.dtype, -1), int(partition_size),
                                  int(max_context_len), workspace.data_ptr(), ws_bytes,
-                                 _stream(q.device, stream))
+                                 PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
     _check(st, "pa_decode_splitk")
     return out
 

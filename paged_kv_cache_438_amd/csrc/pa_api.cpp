@@ -56,7 +56,7 @@ int check_common(int num_seqs, int num_kv_heads, int head_dim, int block_size,
 int check_decode(const void* out, const void* q, const void* k_pool, const void* v_pool,
                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                  int num_heads, int num_kv_heads, int head_dim, int block_size,
-                 int max_blocks_per_seq, int num_blocks, float scale, int dtype) {
+                 int max_blocks_per_seq, int num_blocks, float scale, int dtype, int flags) {
   int st = check_common(num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, dtype);
   if (st) return st;
@@ -64,6 +64,7 @@ int check_decode(const void* out, const void* q, const void* k_pool, const void*
   if (num_heads % num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
                 num_kv_heads);
+  if (flags & ~PA_FLAG_SHARED_KV) return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
     return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs == 0) return PA_OK;
@@ -80,7 +81,7 @@ pa::DecodeParams make_params(void* out, const void* q, const void* k_pool, const
                              const int32_t* block_tables, const int32_t* context_lens,
                              int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_blocks_per_seq, int num_blocks,
-                             float scale, int dtype) {
+                             float scale, int dtype, int flags) {
   pa::DecodeParams p;
   p.out = out;
   p.q = q;
@@ -100,6 +101,7 @@ pa::DecodeParams make_params(void* out, const void* q, const void* k_pool, const
   p.dtype = dtype;
   p.partition_size = 0;
   p.max_partitions = 1;
+  p.flags = flags;
   return p;
 }
 
@@ -162,15 +164,16 @@ int pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_
 int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
               int num_heads, int num_kv_heads, int head_dim, int block_size,
-              int max_blocks_per_seq, int num_blocks, float scale, int dtype, void* stream) {
+              int max_blocks_per_seq, int num_blocks, float scale, int dtype, int flags,
+              void* stream) {
   int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
-                        dtype);
+                        dtype, flags);
   if (st) return st;
   if (num_seqs == 0) return ok();
   pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                                    num_heads, num_kv_heads, head_dim, block_size,
-                                   max_blocks_per_seq, num_blocks, scale, dtype);
+                                   max_blocks_per_seq, num_blocks, scale, dtype, flags);
   // One partition spanning the longest sequence the tables can describe.
   p.partition_size = (int)(ceil_div64((int64_t)max_blocks_per_seq * block_size, 16) * 16);
   p.max_partitions = 1;
@@ -192,10 +195,10 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
                      int num_heads, int num_kv_heads, int head_dim, int block_size,
                      int max_blocks_per_seq, int num_blocks, float scale, int dtype,
                      int partition_size, int max_context_len, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, int flags, void* stream) {
   int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
-                        dtype);
+                        dtype, flags);
   if (st) return st;
   if (partition_size <= 0 || partition_size % 16 != 0)
     return fail(PA_ERR_INVALID_ARG, "partition_size must be a positive multiple of 16 (got %d)",
@@ -213,7 +216,7 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
   if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                                    num_heads, num_kv_heads, head_dim, block_size,
-                                   max_blocks_per_seq, num_blocks, scale, dtype);
+                                   max_blocks_per_seq, num_blocks, scale, dtype, flags);
   const int parts = (int)ceil_div64(max_context_len, partition_size);
   p.partition_size = partition_size;
   p.max_partitions = parts > 0 ? parts : 1;

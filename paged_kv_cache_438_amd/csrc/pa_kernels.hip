@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_launch.h"
 
 namespace pa {
@@ -136,6 +138,24 @@ __device__ __forceinline__ float row_group_sum(float x) {
   return x;
 }
 
+// 16-byte loads of K/V data.  Streaming loads carry the non-temporal hint:
+// each block is read by one sequence once per call, so keeping it in L2 or
+// the Infinity Cache only displaces other lines.  When blocks are shared by
+// several sequences (aliased table entries) the plain, cached load is used.
+__device__ __forceinline__ uint4 ld16_stream(const uint8_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16_cached(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+  if constexpr (NT) return ld16_stream(p);
+  else return ld16_cached(p);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
@@ -190,6 +210,7 @@ struct KArgs {
   int part_tokens;      // P
   int max_parts;
   float scale_log2;     // scale * log2(e)
+  int streaming;        // nonzero: K/V loads carry the non-temporal hint
 };
 
 // One workgroup = (sequence s, KV head g, chunk of GW query heads, partition p).
@@ -244,41 +265,53 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
   bool bad_block = false;
 
-  for (int st = wave; st < nsteps; st += W) {
-    const int t0 = t_begin + (st << 4);
-    uint4 kr[NL], vr[NL];
+  // Iteration k of this wave handles the 16-token step starting at step_t0(k).
+  const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+  auto step_t0 = [&](int k) { return t_begin + ((wave + k * W) << 4); };
+  // block_size >= 16: a step lies in one block, whose id is read once per step
+  // (a wave-uniform scalar load, issued two steps ahead of its use).
+  auto step_phys = [&](int k) -> int {
+    if constexpr (BIG_BLOCKS) return trow[step_t0(k) >> a.bs_log2];
+    else return 0;
+  };
+  auto load_step_t = [&](auto nt, int k, int phys, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+    constexpr bool NT = decltype(nt)::value;
+    const int t0 = step_t0(k);
     if constexpr (BIG_BLOCKS) {
-      // block_size >= 16 and t0 % 16 == 0: the whole step sits in one block.
-      int phys = trow[t0 >> a.bs_log2];
       if ((unsigned)phys >= (unsigned)a.num_blocks) { bad_block = true; phys = 0; }
       const size_t tile = (size_t)phys * block_bytes + (size_t)g * tile_bytes;
-      const int row0 = t0 & bs_mask;
+      const uint8_t* kb = a.k_pool + tile + (size_t)(t0 & bs_mask) * ROWB + c * 16;
+      const uint8_t* vb = a.v_pool + tile + (size_t)(t0 & bs_mask) * ROWB + c * 16;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int t = min(t0 + i * RPL + r, t_end - 1);
-        const size_t off = tile + (size_t)(row0 + (t - t0)) * ROWB + c * 16;
-        kr[i] = *reinterpret_cast<const uint4*>(a.k_pool + off);
+        const int dt = min(i * RPL + r, t_end - 1 - t0);   // last valid row past the end
+        kr[i] = ld16<NT>(kb + dt * ROWB);
       }
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int t = min(t0 + i * RPL + r, t_end - 1);
-        const size_t off = tile + (size_t)(row0 + (t - t0)) * ROWB + c * 16;
-        vr[i] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+        const int dt = min(i * RPL + r, t_end - 1 - t0);
+        vr[i] = ld16<NT>(vb + dt * ROWB);
       }
     } else {
       // block_size < 16: each row looks up its own block.
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int t = min(t0 + i * RPL + r, t_end - 1);
-        int phys = trow[t >> a.bs_log2];
-        if ((unsigned)phys >= (unsigned)a.num_blocks) { bad_block = true; phys = 0; }
-        const size_t off = (size_t)phys * block_bytes + (size_t)g * tile_bytes +
+        int ph = trow[t >> a.bs_log2];
+        if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
+        const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
                            (size_t)(t & bs_mask) * ROWB + c * 16;
-        kr[i] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-        vr[i] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+        kr[i] = ld16<NT>(a.k_pool + off);
+        vr[i] = ld16<NT>(a.v_pool + off);
       }
     }
-
+  };
+  auto load_step = [&](int k, int phys, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
+    if (a.streaming) load_step_t(std::true_type{}, k, phys, kr, vr);
+    else load_step_t(std::false_type{}, k, phys, kr, vr);
+  };
+  auto compute_step = [&](int k, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+    const int t0 = step_t0(k);
     float sc[GW][NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -311,6 +344,22 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
     for (int i = 0; i < NL; ++i)
 #pragma unroll
       for (int hh = 0; hh < GW; ++hh) Axpy<DT>::run(acc[hh], sc[hh][i], vr[i]);
+  };
+
+  // Two register buffers: the loads of step k+1 are in flight while step k
+  // is computed.
+  uint4 kA[NL], vA[NL], kB[NL], vB[NL];
+  int physA = 0, physB = 0;
+  if (nk > 0) { physA = step_phys(0); load_step(0, physA, kA, vA); }
+  if (nk > 1) physB = step_phys(1);
+  for (int k = 0; k < nk; k += 2) {
+    if (k + 1 < nk) load_step(k + 1, physB, kB, vB);
+    if (k + 2 < nk) physA = step_phys(k + 2);
+    compute_step(k, kA, vA);
+    if (k + 1 >= nk) break;
+    if (k + 2 < nk) load_step(k + 2, physA, kA, vA);
+    if (k + 3 < nk) physB = step_phys(k + 3);
+    compute_step(k + 1, kB, vB);
   }
 
   // Merge the row groups of this wave.
@@ -441,30 +490,37 @@ int ilog2(int x) {
   return r;
 }
 
-constexpr int kWaves = 4;
-
-template <int DT, int D, int GW, bool BIG>
-hipError_t launch_decode_t(const KArgs& ka, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_decode<DT, D, kWaves, GW, BIG>), dim3(grid), dim3(kWaves * 64), 0, st, ka);
+template <int DT, int D, int W, int GW>
+hipError_t launch_decode_t(const KArgs& ka, bool big, int grid, hipStream_t st) {
+  if (big) hipLaunchKernelGGL((k_decode<DT, D, W, GW, true>), dim3(grid), dim3(W * 64), 0, st, ka);
+  else hipLaunchKernelGGL((k_decode<DT, D, W, GW, false>), dim3(grid), dim3(W * 64), 0, st, ka);
   return hipGetLastError();
 }
 
+// Waves per workgroup: 16 only for one query head per wave and rows of at
+// most 256 bytes (the two register buffers then fit in 128 VGPRs), else 8 or 4.
 template <int DT, int D>
-hipError_t dispatch_gw(const KArgs& ka, int gw, bool big, int grid, hipStream_t st) {
+hipError_t dispatch_gw(const KArgs& ka, int gw, int waves, bool big, int grid, hipStream_t st) {
   switch (gw) {
-    case 1: return big ? launch_decode_t<DT, D, 1, true>(ka, grid, st)
-                       : launch_decode_t<DT, D, 1, false>(ka, grid, st);
-    case 2: return big ? launch_decode_t<DT, D, 2, true>(ka, grid, st)
-                       : launch_decode_t<DT, D, 2, false>(ka, grid, st);
-    default: return big ? launch_decode_t<DT, D, 4, true>(ka, grid, st)
-                        : launch_decode_t<DT, D, 4, false>(ka, grid, st);
+    case 1:
+      if constexpr (D * Elem<DT>::bytes <= 256)
+        if (waves >= 16) return launch_decode_t<DT, D, 16, 1>(ka, big, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 1>(ka, big, grid, st);
+      return launch_decode_t<DT, D, 4, 1>(ka, big, grid, st);
+    case 2:
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 2>(ka, big, grid, st);
+      return launch_decode_t<DT, D, 4, 2>(ka, big, grid, st);
+    default:
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 4>(ka, big, grid, st);
+      return launch_decode_t<DT, D, 4, 4>(ka, big, grid, st);
   }
 }
 
 template <int DT>
-hipError_t dispatch_d(const KArgs& ka, int d, int gw, bool big, int grid, hipStream_t st) {
-  return d == 64 ? dispatch_gw<DT, 64>(ka, gw, big, grid, st)
-                 : dispatch_gw<DT, 128>(ka, gw, big, grid, st);
+hipError_t dispatch_d(const KArgs& ka, int d, int gw, int waves, bool big, int grid,
+                      hipStream_t st) {
+  return d == 64 ? dispatch_gw<DT, 64>(ka, gw, waves, big, grid, st)
+                 : dispatch_gw<DT, 128>(ka, gw, waves, big, grid, st);
 }
 
 template <int DT>
@@ -505,15 +561,23 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.part_tokens = p.partition_size;
   ka.max_parts = p.max_partitions;
   ka.scale_log2 = p.scale * kLog2e;
+  ka.streaming = (p.flags & kFlagSharedKV) ? 0 : 1;
   const bool big = p.block_size >= 16;
+  // A single pass gives each workgroup a whole sequence: many waves shorten
+  // its critical path and let the dispatcher balance ragged lengths.  A
+  // partition of P tokens has P/16 steps; keep at least four per wave.
+  int waves;
+  const int row_bytes = p.head_dim * (p.dtype == kF32 ? 4 : 2);
+  if (p.workspace == nullptr) waves = gw == 1 && row_bytes <= 256 ? 16 : 8;
+  else waves = p.partition_size >= 512 ? 8 : 4;
   const long long grid = (long long)ka.chunks * p.num_kv_heads * p.num_seqs * p.max_partitions;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
   hipError_t e;
   switch (p.dtype) {
-    case kF32: e = dispatch_d<kF32>(ka, p.head_dim, gw, big, (int)grid, stream); break;
-    case kF16: e = dispatch_d<kF16>(ka, p.head_dim, gw, big, (int)grid, stream); break;
-    default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, big, (int)grid, stream); break;
+    case kF32: e = dispatch_d<kF32>(ka, p.head_dim, gw, waves, big, (int)grid, stream); break;
+    case kF16: e = dispatch_d<kF16>(ka, p.head_dim, gw, waves, big, (int)grid, stream); break;
+    default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, waves, big, (int)grid, stream); break;
   }
   if (e != hipSuccess || p.workspace == nullptr) return e;
 

@@ -10,6 +10,9 @@ namespace pa {
 
 enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
+// Decode flag bits (PA_FLAG_* in pa.h).
+constexpr int kFlagSharedKV = 1;
+
 struct DecodeParams {
   void* out;
   const void* q;
@@ -29,6 +32,7 @@ struct DecodeParams {
   int dtype;
   int partition_size;      // tokens per partition (multiple of 16)
   int max_partitions;      // partitions per sequence covered by the grid
+  int flags;               // PA_FLAG_* bits
 };
 
 struct CacheWriteParams {

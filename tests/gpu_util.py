@@ -53,15 +53,16 @@ class DevCase:
         self.k_new = dev_array(c.k_new, dt)
         self.v_new = dev_array(c.v_new, dt)
 
-    def decode(self, entry: str, partition_size: int = None, scale=None):
+    def decode(self, entry: str, partition_size: int = None, scale=None, shared_kv=False):
         sc = float(self.c.scale) if scale is None else scale
         if entry == "single":
-            return pa.pa_decode(self.q, self.k_pool, self.v_pool, self.tables, self.lens, scale=sc)
+            return pa.pa_decode(self.q, self.k_pool, self.v_pool, self.tables, self.lens, scale=sc,
+                                shared_kv=shared_kv)
         P = partition_size or 256
         return pa.pa_decode_splitk(self.q, self.k_pool, self.v_pool, self.tables, self.lens,
                                    partition_size=P,
                                    max_context_len=int(self.c.context_lens.max(initial=0)),
-                                   scale=sc)
+                                   scale=sc, shared_kv=shared_kv)
 
     def cache_write(self):
         pa.pa_cache_write(self.k_pool, self.v_pool, self.k_new, self.v_new, self.tables, self.lens)

@@ -43,10 +43,11 @@ P = 0x1000
 
 def _decode(lib, **kw):
     a = dict(out=P, q=P, k=P, v=P, tb=P, ln=P, B=4, Hq=8, Hkv=2, d=128, bs=16, MB=8, NB=64,
-             scale=0.088, dtype=1)
+             scale=0.088, dtype=1, flags=0)
     a.update(kw)
     return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["tb"], a["ln"], a["B"], a["Hq"],
-                         a["Hkv"], a["d"], a["bs"], a["MB"], a["NB"], a["scale"], a["dtype"], None)
+                         a["Hkv"], a["d"], a["bs"], a["MB"], a["NB"], a["scale"], a["dtype"],
+                         a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -54,7 +55,7 @@ def _decode(lib, **kw):
     (dict(dtype=7), 3), (dict(Hq=6, Hkv=4), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
     (dict(B=-1), 2), (dict(MB=0), 2), (dict(NB=0), 2), (dict(scale=float("nan")), 2),
     (dict(scale=float("inf")), 2), (dict(q=0), 1), (dict(out=0), 1), (dict(tb=0), 1),
-    (dict(k=P + 4), 2), (dict(out=P + 2), 2),
+    (dict(k=P + 4), 2), (dict(out=P + 2), 2), (dict(flags=2), 2), (dict(flags=-1), 2),
 ])
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -83,10 +84,10 @@ def test_splitk_workspace_sizing_and_rejects(lib):
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 24) == 0
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 96, 2048, 256) == 0
 
-    def call(P_=256, maxlen=100, ws=P, wsb=None):
+    def call(P_=256, maxlen=100, ws=P, wsb=None, flags=0):
         wsb = need if wsb is None else wsb
         return lib.pa_decode_splitk(P, P, P, P, P, P, 64, 32, 32, 128, 16, 128, 9000, 0.088, 1,
-                                    P_, maxlen, ws, wsb, None)
+                                    P_, maxlen, ws, wsb, flags, None)
 
     assert call(P_=24) == 2
     assert call(P_=0) == 2
@@ -96,6 +97,7 @@ def test_splitk_workspace_sizing_and_rejects(lib):
     assert call(wsb=small - 1) == 4
     assert call(ws=0) == 4
     assert call(ws=P + 4, wsb=small) == 2
+    assert call(flags=4, wsb=small) == 2
 
 
 def test_check_inputs_host(lib):

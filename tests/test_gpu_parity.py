@@ -182,6 +182,19 @@ def test_shared_prefix_equals_duplicated_bitwise():
         assert host_bits(a.decode(entry, P)).tobytes() == host_bits(b.decode(entry, P)).tobytes()
 
 
+@pytest.mark.parametrize("w", [small_variant(SHARED_PREFIX), small_variant(GQA70B), TINY],
+                         ids=lambda w: w.name)
+def test_shared_kv_flag_changes_no_bits(w):
+    """The cache-policy flag selects streaming or cached loads only."""
+    c = make_case(w)
+    d = DevCase(c)
+    for entry, P in (("single", None), ("splitk", 32)):
+        note(f"shared_kv flag: {w.name} entry={entry}")
+        a = host_bits(d.decode(entry, P, shared_kv=False)).tobytes()
+        b = host_bits(d.decode(entry, P, shared_kv=True)).tobytes()
+        assert a == b
+
+
 def test_rerun_bitwise_deterministic():
     c = make_case(small_variant(GQA70B))
     d = DevCase(c)
@@ -291,9 +304,10 @@ def test_full_size_sampled(name):
     d = DevCase(c)
     if w.cache_write:
         d.cache_write()         # rewrites each newest token with its own bytes
+    shared = c.shared_groups is not None
     for entry, P in entries:
-        note(f"full: {name} entry={entry} P={P} sampled pairs={len(pairs)}")
-        got = host_f64(d.decode(entry, P))
+        note(f"full: {name} entry={entry} P={P} shared_kv={shared} sampled pairs={len(pairs)}")
+        got = host_f64(d.decode(entry, P, shared_kv=shared))
         torch.cuda.synchronize()
         assert np.all(np.isfinite(got)), "non-finite output at full size"
         idx = tuple(np.array(pairs).T)
