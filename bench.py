@@ -109,6 +109,10 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cached", action="store_true",
+                    help="plain cached K/V loads (the shared-blocks policy) even without sharing")
+    ap.add_argument("--valu-only", action="store_true",
+                    help="grouped heads on the vector ALUs instead of the matrix cores")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run torch copies of this many MiB "
                          "(calibrates HBM byte counters under rocprofv3 --pmc)")
@@ -173,14 +177,16 @@ def main() -> int:
         need = pa.pa_decode_splitk_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, maxlen, P)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-    shared = case.shared_groups is not None      # tables alias a group's prompt blocks
+    shared = case.shared_groups is not None or args.cached   # keep K/V loads cached
 
     def decode():
         if entry == "single":
-            pa.pa_decode(q, kp, vp, tb, ln, scale=scale, out=out, shared_kv=shared)
+            pa.pa_decode(q, kp, vp, tb, ln, scale=scale, out=out, shared_kv=shared,
+                         valu_only=args.valu_only)
         else:
             pa.pa_decode_splitk(q, kp, vp, tb, ln, partition_size=P, max_context_len=maxlen,
-                                scale=scale, out=out, workspace=ws, shared_kv=shared)
+                                scale=scale, out=out, workspace=ws, shared_kv=shared,
+                                valu_only=args.valu_only)
 
     def step():
         pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
@@ -241,6 +247,7 @@ def main() -> int:
         "config": {"workload": w.name, "description": w.description, "seed": case.seed,
                    "entry": "pa_decode" if entry == "single" else "pa_decode_splitk",
                    "partition_size": P, "accumulate": "f32", "shared_kv_flag": shared,
+                   "valu_only": bool(args.valu_only),
                    "global_batch": w.num_seqs, "kv_tokens": tokens,
                    "step": "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
         "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),

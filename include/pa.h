@@ -74,6 +74,11 @@ typedef enum {
  *   non-temporal hint: each block is read once per call and would only
  *   displace other cache lines.  The flag changes speed, never results. */
 #define PA_FLAG_SHARED_KV 1
+/* PA_FLAG_VALU_ONLY: compute grouped query heads (num_heads > num_kv_heads,
+ *   fp16/bf16) on the vector ALUs instead of the matrix cores.  Both paths
+ *   accumulate in fp32 and meet the same error bounds; their results may
+ *   differ in the last bits.  Meant for cross-checks and measurement. */
+#define PA_FLAG_VALU_ONLY 2
 
 /* Supported shapes: head_dim in {64, 128}; block_size a power of two in
  * [1, 1024]; num_heads a multiple of num_kv_heads; dtype one of pa_dtype. */
@@ -123,7 +128,8 @@ int pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_
  * `dtype` (nearest-even).  L = 0 gives a zero row.  `scale` is usually
  * 1/sqrt(head_dim).  `out` must not overlap any input.
  *
- * `flags` is 0 or PA_FLAG_SHARED_KV; other bits are rejected.
+ * `flags` is a combination of PA_FLAG_SHARED_KV and PA_FLAG_VALU_ONLY;
+ * other bits are rejected.
  *
  * One launch; no workspace.  Device contract: 0 <= L <= max_blocks_per_seq *
  * block_size and 0 <= block_tables[s][i] < num_blocks for i < ceil(L/bs);

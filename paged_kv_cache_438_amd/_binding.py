@@ -18,6 +18,7 @@ HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "pa.h"
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_FLAG_SHARED_KV = 1
+PA_FLAG_VALU_ONLY = 2
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 _c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
@@ -137,6 +138,10 @@ def pa_cache_write(k_pool: torch.Tensor, v_pool: torch.Tensor, k_new: torch.Tens
     _check(st, "pa_cache_write")
 
 
+def _flags(shared_kv: bool, valu_only: bool) -> int:
+    return (PA_FLAG_SHARED_KV if shared_kv else 0) | (PA_FLAG_VALU_ONLY if valu_only else 0)
+
+
 def _decode_args(q, k_pool, v_pool, block_tables, context_lens, scale, out):
     for n, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
         _dev(t, n)
@@ -160,16 +165,18 @@ def _decode_args(q, k_pool, v_pool, block_tables, context_lens, scale, out):
 def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor,
               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-              shared_kv: bool = False, stream=None) -> torch.Tensor:
+              shared_kv: bool = False, valu_only: bool = False, stream=None) -> torch.Tensor:
     """Single-pass paged decode attention; returns ``out`` [num_seqs][num_heads][head_dim].
     ``shared_kv``: some blocks appear in several sequences' tables (keeps K/V
-    loads cached instead of streaming); results are identical either way."""
+    loads cached instead of streaming); results are identical either way.
+    ``valu_only``: grouped heads on the vector ALUs instead of the matrix
+    cores (cross-checks and measurement)."""
     out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
                                                            context_lens, scale, out)
     st = load().pa_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                           block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, d, bs,
                           MB, NB, scale, _DTYPES.get(q.dtype, -1),
-                          PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
+                          _flags(shared_kv, valu_only), _stream(q.device, stream))
     _check(st, "pa_decode")
     return out
 
@@ -185,7 +192,7 @@ def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                      partition_size: int, max_context_len: int,
                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, shared_kv: bool = False,
-                     stream=None) -> torch.Tensor:
+                     valu_only: bool = False, stream=None) -> torch.Tensor:
     """Split-K paged decode attention (partition pass + reduce pass)."""
     out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
                                                            context_lens, scale, out)
@@ -199,7 +206,7 @@ def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                                  context_lens.data_ptr(), B, Hq, Hkv, d, bs, MB, NB, scale,
                                  _DTYPES.get(q.dtype, -1), int(partition_size),
                                  int(max_context_len), workspace.data_ptr(), ws_bytes,
-                                 PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
+                                 _flags(shared_kv, valu_only), _stream(q.device, stream))
     _check(st, "pa_decode_splitk")
     return out
 

@@ -64,7 +64,7 @@ int check_decode(const void* out, const void* q, const void* k_pool, const void*
   if (num_heads % num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
                 num_kv_heads);
-  if (flags & ~PA_FLAG_SHARED_KV) return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & ~(PA_FLAG_SHARED_KV | PA_FLAG_VALU_ONLY)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
     return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs == 0) return PA_OK;

@@ -210,12 +210,100 @@ struct KArgs {
   int part_tokens;      // P
   int max_parts;
   float scale_log2;     // scale * log2(e)
-  int streaming;        // nonzero: K/V loads carry the non-temporal hint
+};
+
+// Software pipeline over a wave's nk steps with two register buffers: the
+// loads of step k+1 are issued before step k is computed.  The steady-state
+// body issues its loads unconditionally, so the wait the compiler places
+// before each compute covers only the older buffer's loads and the newer
+// ones stay in flight.
+// A scheduling barrier after each batch of loads keeps the compiler from
+// sinking them below the compute to shorten register live ranges.
+template <typename Buf, typename LoadF, typename ComputeF>
+__device__ __forceinline__ void run_pipeline(int nk, LoadF&& load, ComputeF&& compute) {
+  if (nk <= 0) return;
+  Buf A, B;
+  load(0, A);
+  int k = 0;
+  for (; k + 2 < nk; k += 2) {
+    load(k + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k, A);
+    load(k + 2, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k + 1, B);
+  }
+  if (k + 1 < nk) {
+    load(k + 1, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k, A);
+    compute(k + 1, B);
+  } else {
+    compute(k, A);
+  }
+}
+
+// The same with three register buffers: steps k+1 and k+2 are in flight
+// while step k is computed (twice the bytes in flight per wave, for kernels
+// whose register use allows few waves per CU).  The last two to four steps
+// run as straight-line code.
+template <typename Buf, typename LoadF, typename ComputeF>
+__device__ __forceinline__ void run_pipeline3(int nk, LoadF&& load, ComputeF&& compute) {
+  if (nk <= 0) return;
+  Buf A, B, C;
+  load(0, A);
+  if (nk == 1) {
+    compute(0, A);
+    return;
+  }
+  load(1, B);
+  int k = 0;
+  for (; k + 4 < nk; k += 3) {        // entry: steps k (A) and k+1 (B) issued
+    load(k + 2, C);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k, A);
+    load(k + 3, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k + 1, B);
+    load(k + 4, B);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k + 2, C);
+  }
+  const int rest = nk - k;            // 2, 3 or 4 steps left, k and k+1 issued
+  if (rest == 2) {
+    compute(k, A);
+    compute(k + 1, B);
+  } else if (rest == 3) {
+    load(k + 2, C);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k, A);
+    compute(k + 1, B);
+    compute(k + 2, C);
+  } else {
+    load(k + 2, C);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k, A);
+    load(k + 3, A);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(k + 1, B);
+    compute(k + 2, C);
+    compute(k + 3, A);
+  }
+}
+
+// Block ids of the steps a wave walks, fetched one step ahead of their use.
+// Blocks of at least 16 tokens: a 16-token step lies in one block, whose id is
+// a wave-uniform scalar load.  Smaller blocks: every lane looks up the block
+// of each of its NR rows (vector loads).
+template <bool BIG_BLOCKS, int NR>
+struct BlockIds {
+  int cur[BIG_BLOCKS ? 1 : NR];
+  int nxt[BIG_BLOCKS ? 1 : NR];
 };
 
 // One workgroup = (sequence s, KV head g, chunk of GW query heads, partition p).
 // Its W waves take the partition's 16-token steps round-robin.
-template <int DT, int D, int W, int GW, bool BIG_BLOCKS>
+template <int DT, int D, int W, int GW, bool BIG_BLOCKS, bool NT>
 __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int ROWB = D * EB;           // bytes per token row of one head
@@ -226,7 +314,7 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   static_assert(LPR >= 4 && LPR <= 32 && RPL * LPR == 64 && NL * RPL == 16, "row shape");
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPR;              // row group
   const int c = lane % LPR;              // 16-byte slice within the row
 
@@ -268,16 +356,25 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   // Iteration k of this wave handles the 16-token step starting at step_t0(k).
   const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
   auto step_t0 = [&](int k) { return t_begin + ((wave + k * W) << 4); };
-  // block_size >= 16: a step lies in one block, whose id is read once per step
-  // (a wave-uniform scalar load, issued two steps ahead of its use).
-  auto step_phys = [&](int k) -> int {
-    if constexpr (BIG_BLOCKS) return trow[step_t0(k) >> a.bs_log2];
-    else return 0;
-  };
-  auto load_step_t = [&](auto nt, int k, int phys, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
-    constexpr bool NT = decltype(nt)::value;
+  BlockIds<BIG_BLOCKS, NL> ids;
+  // Fetch the block ids of step k into ids.nxt.
+  auto fetch_ids = [&](int k) {
     const int t0 = step_t0(k);
     if constexpr (BIG_BLOCKS) {
+      ids.nxt[0] = trow[t0 >> a.bs_log2];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) ids.nxt[i] = trow[min(t0 + i * RPL + r, t_end - 1) >> a.bs_log2];
+    }
+  };
+  struct Buf { uint4 k[NL], v[NL]; };
+  auto load_step = [&](int k, Buf& b) {
+    const int t0 = step_t0(k);
+#pragma unroll
+    for (int i = 0; i < (BIG_BLOCKS ? 1 : NL); ++i) ids.cur[i] = ids.nxt[i];
+    fetch_ids(k + 1 < nk ? k + 1 : k);     // unconditional: no branch around loads
+    if constexpr (BIG_BLOCKS) {
+      int phys = ids.cur[0];
       if ((unsigned)phys >= (unsigned)a.num_blocks) { bad_block = true; phys = 0; }
       const size_t tile = (size_t)phys * block_bytes + (size_t)g * tile_bytes;
       const uint8_t* kb = a.k_pool + tile + (size_t)(t0 & bs_mask) * ROWB + c * 16;
@@ -285,32 +382,27 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int dt = min(i * RPL + r, t_end - 1 - t0);   // last valid row past the end
-        kr[i] = ld16<NT>(kb + dt * ROWB);
+        b.k[i] = ld16<NT>(kb + dt * ROWB);
       }
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int dt = min(i * RPL + r, t_end - 1 - t0);
-        vr[i] = ld16<NT>(vb + dt * ROWB);
+        b.v[i] = ld16<NT>(vb + dt * ROWB);
       }
     } else {
-      // block_size < 16: each row looks up its own block.
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int t = min(t0 + i * RPL + r, t_end - 1);
-        int ph = trow[t >> a.bs_log2];
+        int ph = ids.cur[i];
         if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
         const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
                            (size_t)(t & bs_mask) * ROWB + c * 16;
-        kr[i] = ld16<NT>(a.k_pool + off);
-        vr[i] = ld16<NT>(a.v_pool + off);
+        b.k[i] = ld16<NT>(a.k_pool + off);
+        b.v[i] = ld16<NT>(a.v_pool + off);
       }
     }
   };
-  auto load_step = [&](int k, int phys, uint4 (&kr)[NL], uint4 (&vr)[NL]) {
-    if (a.streaming) load_step_t(std::true_type{}, k, phys, kr, vr);
-    else load_step_t(std::false_type{}, k, phys, kr, vr);
-  };
-  auto compute_step = [&](int k, const uint4 (&kr)[NL], const uint4 (&vr)[NL]) {
+  auto compute_step = [&](int k, const Buf& b) {
     const int t0 = step_t0(k);
     float sc[GW][NL];
 #pragma unroll
@@ -318,7 +410,7 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
       const bool valid = t0 + i * RPL + r < t_end;
 #pragma unroll
       for (int hh = 0; hh < GW; ++hh) {
-        const float z = row_group_sum<LPR>(dot16<DT>(kr[i], qv[hh], 0.f)) * a.scale_log2;
+        const float z = row_group_sum<LPR>(dot16<DT>(b.k[i], qv[hh], 0.f)) * a.scale_log2;
         sc[hh][i] = valid ? z : -INFINITY;
       }
     }
@@ -343,24 +435,11 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
 #pragma unroll
     for (int i = 0; i < NL; ++i)
 #pragma unroll
-      for (int hh = 0; hh < GW; ++hh) Axpy<DT>::run(acc[hh], sc[hh][i], vr[i]);
+      for (int hh = 0; hh < GW; ++hh) Axpy<DT>::run(acc[hh], sc[hh][i], b.v[i]);
   };
 
-  // Two register buffers: the loads of step k+1 are in flight while step k
-  // is computed.
-  uint4 kA[NL], vA[NL], kB[NL], vB[NL];
-  int physA = 0, physB = 0;
-  if (nk > 0) { physA = step_phys(0); load_step(0, physA, kA, vA); }
-  if (nk > 1) physB = step_phys(1);
-  for (int k = 0; k < nk; k += 2) {
-    if (k + 1 < nk) load_step(k + 1, physB, kB, vB);
-    if (k + 2 < nk) physA = step_phys(k + 2);
-    compute_step(k, kA, vA);
-    if (k + 1 >= nk) break;
-    if (k + 2 < nk) load_step(k + 2, physA, kA, vA);
-    if (k + 3 < nk) physB = step_phys(k + 3);
-    compute_step(k + 1, kB, vB);
-  }
+  if (nk > 0) fetch_ids(0);
+  run_pipeline<Buf>(nk, load_step, compute_step);
 
   // Merge the row groups of this wave.
 #pragma unroll
@@ -417,6 +496,384 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
       if (poisoned) { asum = __builtin_nanf(""); lsum = __builtin_nanf(""); }
       a.ws_acc[slot * D + e] = asum;
       if (e == 0) a.ws_ml[slot] = make_float2(M, lsum);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Grouped-query decode on the matrix cores.
+//
+// When several query heads share a KV head, q.K^T and p.V are small dense
+// contractions: per 16-token step, S^T = K Q^T is (16 tokens x d) . (d x heads)
+// and O^T += V^T P^T is (d x 16 tokens) . (16 tokens x heads).  On the VALU
+// path every K row needs a 16-lane DPP reduction per query head and every V
+// element G fmas; here both products run on MFMA and the VALU only does the
+// softmax and one register transpose of V.
+//
+// Lane layout of a 16x16 MFMA (wave64): operand lane l holds row/column
+// l % 16 and the slice of the contraction index owned by lane group
+// l / 16; the result lane l holds column l % 16, rows 4*(l/16) .. +3.
+//
+//  * S^T = K . Q^T with v_mfma_f32_16x16x32 (one per 32 head-dim elements):
+//    lane l reads 16 bytes of token l%16 (chunk 4i + l/16 of its row for
+//    product i) and the same chunk of query head l%16.  Both operands use the
+//    same head-dim order, so the sum is the ordinary dot product.
+//  * The result gives lane l the scores of head n = l%16 for tokens
+//    4*(l/16) + r, r = 0..3: exactly the operand layout of P^T in the next
+//    product, so the softmax weights never move between lanes.
+//  * O^T += V^T . P^T with v_mfma_f32_16x16x16 (one per 16 head-dim
+//    elements).  V^T's operand wants four consecutive tokens of one head-dim
+//    element per lane, but memory holds rows; lane 4q + a of quad q reads 16
+//    bytes of token 4*(l/16) + a and the quad transposes its 32-bit words
+//    with two DPP butterfly stages, after which each lane holds two head-dim
+//    elements for the quad's four tokens (two output tiles).
+//  * The weights p are split into a high part (exact in the 16-bit element
+//    type) and the remainder, each multiplied with V, so the weights keep
+//    about 14 significant bits while the accumulation stays in fp32.
+//
+// Result lane l, tile 2i+e, register r holds head l%16 at head-dim element
+// 32i + 8*(l/16) + 2r + e: each lane owns 8 consecutive elements per i.
+// Heads of the 16 columns beyond the group are zero queries; their results
+// are discarded.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Mma;
+template <> struct Mma<kBF16> {
+  static __device__ __forceinline__ f32x4_t qk(uint4 k, uint4 q, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k),
+                                                   __builtin_bit_cast(bf16x8_t, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(uint2 v, uint2 p, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v),
+                                                     __builtin_bit_cast(bf16x4_t, p), c, 0, 0, 0);
+  }
+  // Two weights -> packed high parts (bf16 truncation, exact) and packed
+  // remainders (bf16 truncation of p - high).
+  static __device__ __forceinline__ void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
+    const uint32_t r0 = __float_as_uint(p0 - __uint_as_float(h0));
+    const uint32_t r1 = __float_as_uint(p1 - __uint_as_float(h1));
+    hi = __builtin_amdgcn_perm(h1, h0, 0x07060302u);
+    lo = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
+  }
+};
+template <> struct Mma<kF16> {
+  static __device__ __forceinline__ f32x4_t qk(uint4 k, uint4 q, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, k),
+                                                  __builtin_bit_cast(f16x8_t, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(uint2 v, uint2 p, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, v),
+                                                 __builtin_bit_cast(f16x4_t, p), c, 0, 0, 0);
+  }
+  // fp16 high parts rounded toward zero, then the rounded remainders.
+  static __device__ __forceinline__ void split2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+    const fp16x2_t h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+    const fp16x2_t r = __builtin_amdgcn_cvt_pkrtz(p0 - (float)h.x, p1 - (float)h.y);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+
+// 4x4 transpose of 32-bit words across the lanes of a quad: on entry lane a
+// holds words w[0..3]; on exit w[j] is the word a that lane j held.  Stage 1
+// swaps the off-diagonal 2x2 blocks between lanes a and a^2, stage 2
+// transposes each 2x2 block between lanes a and a^1.
+__device__ __forceinline__ void quad_transpose(uint32_t (&w)[4], int a) {
+  const bool hi_half = a & 2, odd = a & 1;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t got = dpp_u32<0x4E>(hi_half ? w[j] : w[2 + j]);   // quad_perm [2,3,0,1]
+    if (hi_half) w[j] = got; else w[2 + j] = got;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t got = dpp_u32<0xB1>(odd ? w[2 * j] : w[2 * j + 1]);  // quad_perm [1,0,3,2]
+    if (odd) w[2 * j] = got; else w[2 * j + 1] = got;
+  }
+}
+
+// K/V reach the matrix-core operands through LDS.  Each wave owns two slots
+// of one 16-token step each (K tile then V tile).  Direct-to-LDS loads
+// (global_load_lds_dwordx4) fill a slot without passing through registers,
+// so both slots can be in flight while the wave computes from registers:
+// the bytes in flight per CU are bounded by LDS, not by the register file.
+// Every load instruction reads whole rows (LPR lanes per row, 16 bytes
+// each), i.e. whole cache lines.  Inside a slot, chunk c of row r is stored
+// at position c ^ swz(r): the operand reads below (16 rows at one chunk for
+// K, four rows at four chunks for V) then hit 16 distinct bank groups.
+//
+// The loads go through the compiler builtin (which manages M0) but the LDS
+// reads of the slots are written as inline assembly, with explicit waits:
+// vmcnt(n) for the slot's loads, lgkmcnt(0) before a slot is refilled.  The
+// compiler would otherwise wait for every outstanding direct-to-LDS load
+// before any LDS read, which serialises the two slots.
+__device__ __forceinline__ uint4 lds_read16(uint32_t addr) {
+  uint4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+template <bool NT>
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
+  // aux bit 1 = slc: the streaming (non-temporal) policy of ld16_stream
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, NT ? 2 : 0);
+}
+
+// Block tables are read-only for the whole kernel: reading them through the
+// constant address space lets wave-uniform lookups stay scalar loads even
+// though the inline assembly above is marked as touching memory.
+typedef const int32_t __attribute__((address_space(4)))* const_i32_ptr;
+
+// Position of 16-byte chunk c of row r (r < 16) inside a slot row.
+template <int D>
+__device__ __forceinline__ int swz_pos(int c, int r) {
+  if constexpr (D == 128) return c ^ (((r & 3) << 2) | (r >> 2));
+  else return c ^ ((r >> 1) & 7);
+}
+
+// One workgroup = (sequence s, KV head g, chunk of up to 16 query heads,
+// partition p); its W waves take the partition's 16-token steps round-robin.
+// Dynamic LDS: W * 4 * 16 * D * 2 bytes (two slots of K and V tiles per
+// wave), reused after the loop for the merge of the waves.
+template <int DT, int D, int W, bool BIG_BLOCKS, bool NT>
+__global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
+  constexpr int EB = 2;
+  constexpr int ROWB = D * EB;
+  constexpr int LPR = ROWB / 16;      // lanes (16-byte chunks) per row
+  constexpr int RPI = 64 / LPR;       // rows per load instruction
+  constexpr int NDMA = 16 / RPI;      // load instructions per 16-row tile
+  constexpr int TILE = 16 * ROWB;
+  constexpr int SLOT = 2 * TILE;      // K tile, V tile
+  constexpr int NI = D / 32;          // K (and V) operands of 16 bytes per lane per step
+  constexpr int NTILE = D / 16;       // output tiles of 16 head-dim elements
+  static_assert(NI * 32 == D && RPI * ROWB == 1024, "head_dim");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;            // head column
+  const int lg = lane >> 4;           // lane group: owns tokens 4*lg .. 4*lg+3
+  const int qa = lane & 3;            // position in the quad
+  const int qb = (lane >> 2) & 3;     // quad index inside the lane group
+
+  int wg = blockIdx.x;
+  const int ch = wg % a.chunks;  wg /= a.chunks;
+  const int g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
+  const int s = wg % a.num_seqs;
+  const int p = wg / a.num_seqs;
+
+  const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
+  const bool direct = sp.nparts <= 1;
+  if (p >= (sp.nparts > 1 ? sp.nparts : 1)) return;
+  const int t_begin = p * a.part_tokens;
+  const int t_end = min(t_begin + a.part_tokens, sp.len);
+  const int nsteps = t_end > t_begin ? (t_end - t_begin + 15) >> 4 : 0;
+
+  const int h0 = g * a.group + ch * 16;
+  const int nh = min(16, a.group - ch * 16);     // real heads in this chunk
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+  uint8_t* wave_lds = s_dyn + wave * 2 * SLOT;
+  const uint32_t wave_lds_addr = (uint32_t)(uintptr_t)wave_lds;
+
+  // Q^T operand: head h0+n, chunk 4i + lg of its row (zero beyond the group).
+  // Waited for here, before any direct-to-LDS load is issued.
+  uint4 qv[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    qv[i] = make_uint4(0, 0, 0, 0);
+    if (n < nh)
+      qv[i] = *reinterpret_cast<const uint4*>(
+          a.q + ((size_t)(s * a.num_heads + h0 + n) * D) * EB + (4 * i + lg) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    asm volatile("" : "+v"(qv[i].x), "+v"(qv[i].y), "+v"(qv[i].z), "+v"(qv[i].w));
+
+  f32x4_t acc[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kEmptyMax, lsum = 0.f;
+
+  const int bs_mask = (1 << a.bs_log2) - 1;
+  const size_t tile_bytes = (size_t)ROWB << a.bs_log2;
+  const size_t block_bytes = tile_bytes * a.num_kv_heads;
+  const const_i32_ptr trow = (const_i32_ptr)(a.tables + (size_t)s * a.max_blocks);
+  bool bad_block = false;
+
+  const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+  auto step_t0 = [&](int k) { return t_begin + ((wave + k * W) << 4); };
+  // Row of the step this lane loads with instruction j (clamped to the last
+  // valid row past the end), and its position in the slot row.
+  const int lrow = lane / LPR;
+  const int lpos = lane % LPR;
+  BlockIds<BIG_BLOCKS, NDMA> ids;
+  auto fetch_ids = [&](int k) {
+    const int t0 = step_t0(k);
+    if constexpr (BIG_BLOCKS) {
+      ids.nxt[0] = trow[t0 >> a.bs_log2];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j)
+        ids.nxt[j] = trow[min(t0 + j * RPI + lrow, t_end - 1) >> a.bs_log2];
+    }
+  };
+  auto issue = [&](int k, int slot) {
+    const int t0 = step_t0(k);
+#pragma unroll
+    for (int i = 0; i < (BIG_BLOCKS ? 1 : NDMA); ++i) ids.cur[i] = ids.nxt[i];
+    fetch_ids(k + 1 < nk ? k + 1 : k);
+    uint8_t* dst = wave_lds + slot * SLOT;
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int row = j * RPI + lrow;
+      const int t = min(t0 + row, t_end - 1);
+      int ph = ids.cur[BIG_BLOCKS ? 0 : j];
+      if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
+      const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
+                         (size_t)(t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
+      dma16<NT>(a.k_pool + off, dst + j * 1024);
+      dma16<NT>(a.v_pool + off, dst + TILE + j * 1024);
+    }
+  };
+  struct Ops { uint4 k[NI], v[NI]; };
+  // Operand reads from a slot: K of row n at chunk 4i + lg; V of row
+  // 4*lg + qa at chunk 4i + qb.
+  auto read_ops = [&](int slot) {
+    Ops o;
+    const uint32_t base = wave_lds_addr + slot * SLOT;
+    const int vr = 4 * lg + qa;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      o.k[i] = lds_read16(base + n * ROWB + swz_pos<D>(4 * i + lg, n) * 16);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      o.v[i] = lds_read16(base + TILE + vr * ROWB + swz_pos<D>(4 * i + qb, vr) * 16);
+    return o;
+  };
+  auto compute_step = [&](int k, const Ops& b) {
+    const int t0 = step_t0(k);
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) sc = Mma<DT>::qk(b.k[i], qv[i], sc);
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = (t0 + 4 * lg + r < t_end) ? sc[r] * a.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(z[r] - mn);
+    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {   // wave-uniform skip
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t) acc[t] *= alpha;
+    }
+    uint2 phi, plo;
+    Mma<DT>::split2(pr[0], pr[1], phi.x, plo.x);
+    Mma<DT>::split2(pr[2], pr[3], phi.y, plo.y);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      uint32_t w[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
+      quad_transpose(w, qa);
+      // tile 2i: low halves (element 2*qa of the chunk), tile 2i+1: high halves
+      const uint2 v0 = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                                  __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
+      const uint2 v1 = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                                  __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
+      acc[2 * i] = Mma<DT>::pv(v0, phi, acc[2 * i]);
+      acc[2 * i] = Mma<DT>::pv(v0, plo, acc[2 * i]);
+      acc[2 * i + 1] = Mma<DT>::pv(v1, phi, acc[2 * i + 1]);
+      acc[2 * i + 1] = Mma<DT>::pv(v1, plo, acc[2 * i + 1]);
+    }
+  };
+
+  // Two slots in flight; a slot is refilled as soon as its operands are in
+  // registers.
+  if (nk > 0) {
+    fetch_ids(0);
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+  }
+  for (int k = 0; k < nk; ++k) {
+    const int slot = k & 1;
+    if (k + 1 < nk) wait_vmcnt<2 * NDMA>();   // the younger slot may stay in flight
+    else wait_vmcnt<0>();
+    const Ops ops = read_ops(slot);
+    wait_lgkmcnt0();
+    if (k + 2 < nk) issue(k + 2, slot);
+    compute_step(k, ops);
+  }
+
+  // Sum of weights of head n over the wave's four lane groups.
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  // Merge the waves through LDS (the slots are free once every wave is here:
+  // each wave's last step waited for all of its loads).
+  __syncthreads();
+  float* s_acc = reinterpret_cast<float*>(s_dyn);          // [W][nh][D]
+  float* s_m = s_acc + (size_t)W * nh * D;                // [W][16]
+  float* s_l = s_m + W * 16;                              // [W][16]
+  int* s_bad = reinterpret_cast<int*>(s_l + W * 16);
+  if (threadIdx.x == 0) *s_bad = 0;
+  __syncthreads();
+  if (bad_block) *s_bad = 1;
+  if (n < nh) {
+    float* dst = s_acc + ((size_t)wave * nh + n) * D;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<float2*>(dst + 32 * i + 8 * lg + 2 * r) =
+            make_float2(acc[2 * i][r], acc[2 * i + 1][r]);
+    if (lg == 0) { s_m[wave * 16 + n] = m; s_l[wave * 16 + n] = lsum; }
+  }
+  __syncthreads();
+  const bool poisoned = sp.bad || *s_bad;
+  for (int idx = threadIdx.x; idx < nh * D; idx += W * 64) {
+    const int hh = idx / D, e = idx % D;
+    float M = s_m[hh];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w * 16 + hh]);
+    float ls = 0.f, as = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float f = fast_exp2(s_m[w * 16 + hh] - M);
+      ls += s_l[w * 16 + hh] * f;
+      as += s_acc[((size_t)w * nh + hh) * D + e] * f;
+    }
+    const int h = h0 + hh;
+    if (direct) {
+      float v = ls > 0.f ? as / ls : 0.f;
+      if (poisoned) v = __builtin_nanf("");
+      store_elem<DT>(a.out, (size_t)(s * a.num_heads + h) * D + e, v);
+    } else {
+      const size_t slot = (size_t)(s * a.num_heads + h) * a.max_parts + p;
+      if (poisoned) { as = __builtin_nanf(""); ls = __builtin_nanf(""); }
+      a.ws_acc[slot * D + e] = as;
+      if (e == 0) a.ws_ml[slot] = make_float2(M, ls);
     }
   }
 }
@@ -491,36 +948,63 @@ int ilog2(int x) {
 }
 
 template <int DT, int D, int W, int GW>
-hipError_t launch_decode_t(const KArgs& ka, bool big, int grid, hipStream_t st) {
-  if (big) hipLaunchKernelGGL((k_decode<DT, D, W, GW, true>), dim3(grid), dim3(W * 64), 0, st, ka);
-  else hipLaunchKernelGGL((k_decode<DT, D, W, GW, false>), dim3(grid), dim3(W * 64), 0, st, ka);
+hipError_t launch_decode_t(const KArgs& ka, bool big, bool nt, int grid, hipStream_t st) {
+  const dim3 gd(grid), bd(W * 64);
+  if (big && nt) hipLaunchKernelGGL((k_decode<DT, D, W, GW, true, true>), gd, bd, 0, st, ka);
+  else if (big) hipLaunchKernelGGL((k_decode<DT, D, W, GW, true, false>), gd, bd, 0, st, ka);
+  else if (nt) hipLaunchKernelGGL((k_decode<DT, D, W, GW, false, true>), gd, bd, 0, st, ka);
+  else hipLaunchKernelGGL((k_decode<DT, D, W, GW, false, false>), gd, bd, 0, st, ka);
   return hipGetLastError();
 }
 
 // Waves per workgroup: 16 only for one query head per wave and rows of at
 // most 256 bytes (the two register buffers then fit in 128 VGPRs), else 8 or 4.
 template <int DT, int D>
-hipError_t dispatch_gw(const KArgs& ka, int gw, int waves, bool big, int grid, hipStream_t st) {
+hipError_t dispatch_gw(const KArgs& ka, int gw, int waves, bool big, bool nt, int grid,
+                       hipStream_t st) {
   switch (gw) {
     case 1:
       if constexpr (D * Elem<DT>::bytes <= 256)
-        if (waves >= 16) return launch_decode_t<DT, D, 16, 1>(ka, big, grid, st);
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 1>(ka, big, grid, st);
-      return launch_decode_t<DT, D, 4, 1>(ka, big, grid, st);
+        if (waves >= 16) return launch_decode_t<DT, D, 16, 1>(ka, big, nt, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 1>(ka, big, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 1>(ka, big, nt, grid, st);
     case 2:
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 2>(ka, big, grid, st);
-      return launch_decode_t<DT, D, 4, 2>(ka, big, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 2>(ka, big, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 2>(ka, big, nt, grid, st);
     default:
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 4>(ka, big, grid, st);
-      return launch_decode_t<DT, D, 4, 4>(ka, big, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 4>(ka, big, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 4>(ka, big, nt, grid, st);
   }
 }
 
 template <int DT>
-hipError_t dispatch_d(const KArgs& ka, int d, int gw, int waves, bool big, int grid,
+hipError_t dispatch_d(const KArgs& ka, int d, int gw, int waves, bool big, bool nt, int grid,
                       hipStream_t st) {
-  return d == 64 ? dispatch_gw<DT, 64>(ka, gw, waves, big, grid, st)
-                 : dispatch_gw<DT, 128>(ka, gw, waves, big, grid, st);
+  return d == 64 ? dispatch_gw<DT, 64>(ka, gw, waves, big, nt, grid, st)
+                 : dispatch_gw<DT, 128>(ka, gw, waves, big, nt, grid, st);
+}
+
+template <int DT, int D, int W>
+hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t lds, hipStream_t st) {
+  const dim3 gd(grid), bd(W * 64);
+  if (big && nt) hipLaunchKernelGGL((k_decode_mfma<DT, D, W, true, true>), gd, bd, lds, st, ka);
+  else if (big) hipLaunchKernelGGL((k_decode_mfma<DT, D, W, true, false>), gd, bd, lds, st, ka);
+  else if (nt) hipLaunchKernelGGL((k_decode_mfma<DT, D, W, false, true>), gd, bd, lds, st, ka);
+  else hipLaunchKernelGGL((k_decode_mfma<DT, D, W, false, false>), gd, bd, lds, st, ka);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dispatch_mfma(const KArgs& ka, int d, int waves, bool big, bool nt, int grid,
+                         hipStream_t st) {
+  // Two slots of one 16-token K tile and V tile per wave; the merge of the
+  // waves after the loop reuses them.
+  const size_t lds = (size_t)waves * 2 * 2 * 16 * d * 2;
+  if (d == 64)
+    return waves >= 8 ? launch_mfma_t<DT, 64, 8>(ka, big, nt, grid, lds, st)
+                      : launch_mfma_t<DT, 64, 4>(ka, big, nt, grid, lds, st);
+  return waves >= 8 ? launch_mfma_t<DT, 128, 8>(ka, big, nt, grid, lds, st)
+                    : launch_mfma_t<DT, 128, 4>(ka, big, nt, grid, lds, st);
 }
 
 template <int DT>
@@ -556,12 +1040,17 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.max_blocks = p.max_blocks_per_seq;
   ka.num_blocks = p.num_blocks;
   ka.group = p.num_heads / p.num_kv_heads;
+  // Grouped heads in 16-bit types run on the matrix cores (chunks of up to 16
+  // query heads per workgroup); fp32, single heads, or the VALU-only flag use
+  // the vector path (chunks of GW heads).
+  const bool mfma = p.dtype != kF32 && ka.group >= 2 && !(p.flags & kFlagValuOnly);
   const int gw = ka.group % 4 == 0 ? 4 : (ka.group % 2 == 0 ? 2 : 1);
-  ka.chunks = ka.group / gw;
+  ka.chunks = mfma ? (ka.group + 15) / 16 : ka.group / gw;
   ka.part_tokens = p.partition_size;
   ka.max_parts = p.max_partitions;
   ka.scale_log2 = p.scale * kLog2e;
-  ka.streaming = (p.flags & kFlagSharedKV) ? 0 : 1;
+  // Streaming (non-temporal) K/V loads unless blocks are shared.
+  const bool nt = !(p.flags & kFlagSharedKV);
   const bool big = p.block_size >= 16;
   // A single pass gives each workgroup a whole sequence: many waves shorten
   // its critical path and let the dispatcher balance ragged lengths.  A
@@ -574,10 +1063,16 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
   hipError_t e;
-  switch (p.dtype) {
-    case kF32: e = dispatch_d<kF32>(ka, p.head_dim, gw, waves, big, (int)grid, stream); break;
-    case kF16: e = dispatch_d<kF16>(ka, p.head_dim, gw, waves, big, (int)grid, stream); break;
-    default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, waves, big, (int)grid, stream); break;
+  if (mfma) {
+    const int mw = 4;     // 4 waves x 16 KiB of slots = 64 KiB of LDS per workgroup
+    e = p.dtype == kF16 ? dispatch_mfma<kF16>(ka, p.head_dim, mw, big, nt, (int)grid, stream)
+                        : dispatch_mfma<kBF16>(ka, p.head_dim, mw, big, nt, (int)grid, stream);
+  } else {
+    switch (p.dtype) {
+      case kF32: e = dispatch_d<kF32>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;
+      case kF16: e = dispatch_d<kF16>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;
+      default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;
+    }
   }
   if (e != hipSuccess || p.workspace == nullptr) return e;
 

@@ -12,6 +12,7 @@ enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // Decode flag bits (PA_FLAG_* in pa.h).
 constexpr int kFlagSharedKV = 1;
+constexpr int kFlagValuOnly = 2;
 
 struct DecodeParams {
   void* out;

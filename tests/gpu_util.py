@@ -53,16 +53,17 @@ class DevCase:
         self.k_new = dev_array(c.k_new, dt)
         self.v_new = dev_array(c.v_new, dt)
 
-    def decode(self, entry: str, partition_size: int = None, scale=None, shared_kv=False):
+    def decode(self, entry: str, partition_size: int = None, scale=None, shared_kv=False,
+               valu_only=False):
         sc = float(self.c.scale) if scale is None else scale
         if entry == "single":
             return pa.pa_decode(self.q, self.k_pool, self.v_pool, self.tables, self.lens, scale=sc,
-                                shared_kv=shared_kv)
+                                shared_kv=shared_kv, valu_only=valu_only)
         P = partition_size or 256
         return pa.pa_decode_splitk(self.q, self.k_pool, self.v_pool, self.tables, self.lens,
                                    partition_size=P,
                                    max_context_len=int(self.c.context_lens.max(initial=0)),
-                                   scale=sc, shared_kv=shared_kv)
+                                   scale=sc, shared_kv=shared_kv, valu_only=valu_only)
 
     def cache_write(self):
         pa.pa_cache_write(self.k_pool, self.v_pool, self.k_new, self.v_new, self.tables, self.lens)

@@ -55,7 +55,7 @@ def _decode(lib, **kw):
     (dict(dtype=7), 3), (dict(Hq=6, Hkv=4), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
     (dict(B=-1), 2), (dict(MB=0), 2), (dict(NB=0), 2), (dict(scale=float("nan")), 2),
     (dict(scale=float("inf")), 2), (dict(q=0), 1), (dict(out=0), 1), (dict(tb=0), 1),
-    (dict(k=P + 4), 2), (dict(out=P + 2), 2), (dict(flags=2), 2), (dict(flags=-1), 2),
+    (dict(k=P + 4), 2), (dict(out=P + 2), 2), (dict(flags=4), 2), (dict(flags=-1), 2),
 ])
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status

@@ -116,6 +116,39 @@ def test_decode_edge_lengths(spec):
                 assert np.all(got[s] == 0.0), "empty sequence must give zeros"
 
 
+# ------------------------------------------------------------------ grouped heads: both paths
+GROUPED = [
+    # (name, lens, Hq, Hkv, d, bs, dtype, partition)
+    ("g2_bf16_bs1", (0, 1, 2, 3, 15, 16, 17, 33, 47, 48, 49), 4, 2, 64, 1, "bf16", 16),
+    ("g3_f16_bs4", (0, 5, 16, 17, 64, 90), 6, 2, 64, 4, "f16", 48),
+    ("g8_bf16_bs8", (1, 7, 8, 9, 31, 32, 33, 200), 16, 2, 128, 8, "bf16", 64),
+    ("g8_f16_bs16", (1, 15, 16, 17, 100, 255, 256, 257, 700), 16, 2, 128, 16, "f16", 128),
+    ("g16_bf16_bs16", (3, 16, 40, 129, 300), 32, 2, 128, 16, "bf16", 64),
+    ("g20_f16_bs32", (1, 31, 32, 33, 150), 40, 2, 64, 32, "f16", 64),
+    ("g4_bf16_bs512", (1, 511, 512, 513, 1100), 8, 2, 128, 512, "bf16", 512),
+]
+
+
+@pytest.mark.parametrize("spec", GROUPED, ids=lambda s: s[0])
+def test_grouped_heads_both_paths(spec):
+    """Grouped query heads in 16-bit types run on the matrix cores; the
+    vector-ALU path stays available under a flag.  Both must match the oracle,
+    for group sizes below, at and above the 16 columns of one MFMA tile."""
+    w = edge_workload(*spec)
+    c = make_case(w)
+    ref = _oracle(c)
+    d = DevCase(c)
+    for valu in (False, True):
+        for entry, P in (("single", None), ("splitk", w.partition_size), ("splitk", 16)):
+            note(f"grouped: {w.name} valu_only={valu} entry={entry} P={P} lens={list(w.lengths)}")
+            got = host_f64(d.decode(entry, P, valu_only=valu))
+            torch.cuda.synchronize()
+            _check_close(got, ref, w.dtype, f"{w.name}/valu={valu}/{entry}/{P}")
+            for s_, L in enumerate(w.lengths):
+                if L == 0:
+                    assert np.all(got[s_] == 0.0)
+
+
 # ------------------------------------------------------------------ bit-exact indexing
 def _needle_case(w, seed):
     """Every query is 32*e_0; key component 0 is 0 everywhere except one
@@ -150,9 +183,12 @@ def test_needle_bit_exact(spec):
     c, needles = _needle_case(w, seed=5)
     d = DevCase(c)
     G = w.num_heads // w.num_kv_heads
-    for entry, P in (("single", None), ("splitk", w.partition_size), ("splitk", 16)):
-        note(f"needle: {w.name} entry={entry} P={P} needles={needles}")
-        got = host_bits(d.decode(entry, P))
+    paths = [False, True] if G > 1 and w.dtype != "f32" else [False]
+    for valu, (entry, P) in [(v, e) for v in paths
+                             for e in (("single", None), ("splitk", w.partition_size),
+                                       ("splitk", 16))]:
+        note(f"needle: {w.name} valu_only={valu} entry={entry} P={P} needles={needles}")
+        got = host_bits(d.decode(entry, P, valu_only=valu))
         for s, pos in enumerate(needles):
             if pos < 0:
                 continue
