@@ -204,6 +204,8 @@ struct KArgs {
   const int32_t* lens;
   float* ws_acc;        // [B][Hq][max_parts][D]
   float2* ws_ml;        // [B][Hq][max_parts] of (max, sum)
+  const int* n_units;   // split-K plan: number of (sequence, partition) units
+  const int2* units;    // split-K plan: units, longest first
   int num_seqs, num_heads, num_kv_heads, bs_log2, max_blocks, num_blocks;
   int group;            // query heads per KV head
   int chunks;           // group / GW
@@ -211,6 +213,30 @@ struct KArgs {
   int max_parts;
   float scale_log2;     // scale * log2(e)
 };
+
+// The (KV head, head chunk, sequence, partition) a workgroup works on.
+// Split-K launches follow the plan written by k_plan: workgroup index
+// (unit, KV head, chunk), units longest first, so the dispatcher schedules
+// long pieces before short ones (longest-first list scheduling); workgroups
+// past the plan's unit count exit.  A single pass has one unit per sequence.
+struct Unit {
+  int ch, g, s, p;
+};
+__device__ __forceinline__ bool resolve_unit(const KArgs& a, Unit& u) {
+  int wg = blockIdx.x;
+  u.ch = wg % a.chunks;  wg /= a.chunks;
+  u.g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
+  if (a.units != nullptr) {
+    if (wg >= *a.n_units) return false;
+    const int2 su = a.units[wg];
+    u.s = su.x;
+    u.p = su.y;
+  } else {
+    u.s = wg;
+    u.p = 0;
+  }
+  return true;
+}
 
 // Software pipeline over a wave's nk steps with two register buffers: the
 // loads of step k+1 are issued before step k is computed.  The steady-state
@@ -318,15 +344,11 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   const int r = lane / LPR;              // row group
   const int c = lane % LPR;              // 16-byte slice within the row
 
-  int wg = blockIdx.x;
-  const int ch = wg % a.chunks;  wg /= a.chunks;
-  const int g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
-  const int s = wg % a.num_seqs;
-  const int p = wg / a.num_seqs;
-
+  Unit un;
+  if (!resolve_unit(a, un)) return;
+  const int ch = un.ch, g = un.g, s = un.s, p = un.p;
   const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
   const bool direct = sp.nparts <= 1;    // the only partition writes the output itself
-  if (p >= (sp.nparts > 1 ? sp.nparts : 1)) return;
   const int t_begin = p * a.part_tokens;
   const int t_end = min(t_begin + a.part_tokens, sp.len);
   const int nsteps = t_end > t_begin ? (t_end - t_begin + 15) >> 4 : 0;
@@ -673,39 +695,23 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
   const int qa = lane & 3;            // position in the quad
   const int qb = (lane >> 2) & 3;     // quad index inside the lane group
 
-  int wg = blockIdx.x;
-  const int ch = wg % a.chunks;  wg /= a.chunks;
-  const int g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
-  const int s = wg % a.num_seqs;
-  const int p = wg / a.num_seqs;
-
+  Unit un;
+  if (!resolve_unit(a, un)) return;
+  const int ch = un.ch, g = un.g, s = un.s, p = un.p;
   const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
-  const bool direct = sp.nparts <= 1;
-  if (p >= (sp.nparts > 1 ? sp.nparts : 1)) return;
+  const bool direct = sp.nparts <= 1;    // the only partition writes the output itself
   const int t_begin = p * a.part_tokens;
   const int t_end = min(t_begin + a.part_tokens, sp.len);
   const int nsteps = t_end > t_begin ? (t_end - t_begin + 15) >> 4 : 0;
 
   const int h0 = g * a.group + ch * 16;
   const int nh = min(16, a.group - ch * 16);     // real heads in this chunk
+  uint4 qv[NI];                                  // Q^T operand, loaded below
 
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
   uint8_t* wave_lds = s_dyn + wave * 2 * SLOT;
   const uint32_t wave_lds_addr = (uint32_t)(uintptr_t)wave_lds;
 
-  // Q^T operand: head h0+n, chunk 4i + lg of its row (zero beyond the group).
-  // Waited for here, before any direct-to-LDS load is issued.
-  uint4 qv[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    qv[i] = make_uint4(0, 0, 0, 0);
-    if (n < nh)
-      qv[i] = *reinterpret_cast<const uint4*>(
-          a.q + ((size_t)(s * a.num_heads + h0 + n) * D) * EB + (4 * i + lg) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-    asm volatile("" : "+v"(qv[i].x), "+v"(qv[i].y), "+v"(qv[i].z), "+v"(qv[i].w));
 
   f32x4_t acc[NTILE];
 #pragma unroll
@@ -809,13 +815,39 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
     }
   };
 
+  // Q^T operand: head h0+n, chunk 4i + lg of its row (zero beyond the
+  // group).  Its loads go out between the first and second slot's K/V loads,
+  // so their latency overlaps the first tile's and waiting for them (vmcnt
+  // counts in order) leaves the second slot in flight.
+  auto load_q = [&]() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      qv[i] = make_uint4(0, 0, 0, 0);
+      if (n < nh)
+        qv[i] = *reinterpret_cast<const uint4*>(
+            a.q + ((size_t)(s * a.num_heads + h0 + n) * D) * EB + (4 * i + lg) * 16);
+    }
+  };
+
   // Two slots in flight; a slot is refilled as soon as its operands are in
   // registers.
   if (nk > 0) {
     fetch_ids(0);
     issue(0, 0);
-    if (nk > 1) issue(1, 1);
+    load_q();
+    if (nk > 1) {
+      issue(1, 1);
+      wait_vmcnt<2 * NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  } else {
+    load_q();
+    wait_vmcnt<0>();
   }
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    asm volatile("" : "+v"(qv[i].x), "+v"(qv[i].y), "+v"(qv[i].z), "+v"(qv[i].w));
   for (int k = 0; k < nk; ++k) {
     const int slot = k & 1;
     if (k + 1 < nk) wait_vmcnt<2 * NDMA>();   // the younger slot may stay in flight
@@ -878,6 +910,65 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
   }
 }
 
+struct PArgs {
+  const int32_t* lens;
+  int* n_units;
+  int2* units;          // [num_seqs * max_parts]
+  int num_seqs, part_tokens, max_parts, max_blocks, bs_log2;
+};
+
+// Split-K plan: every sequence contributes ceil(L/P) units (sequence,
+// partition), at least one.  All but the last are full (P tokens); the last
+// holds the remainder.  One workgroup counting-sorts the units by size into
+// 256 buckets, largest first, so the partition kernel's workgroups are
+// dispatched longest first.  The order inside a bucket depends on timing,
+// but no result does: each unit's arithmetic and the reduce are fixed.
+__global__ __launch_bounds__(1024) void k_plan(const PArgs a) {
+  __shared__ int hist[256];
+  __shared__ int wave_tot[4];
+  const int tid = threadIdx.x;
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  auto last_bucket = [&](const SeqParts& sp, int np) {
+    const int size = sp.len - (np - 1) * a.part_tokens;     // 0 for an empty sequence
+    const long long b = ((long long)(a.part_tokens - size) * 256) / a.part_tokens;
+    return (int)(b > 255 ? 255 : b);
+  };
+  for (int s = tid; s < a.num_seqs; s += 1024) {
+    const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
+    const int np = sp.nparts > 1 ? sp.nparts : 1;
+    if (np > 1) atomicAdd(&hist[0], np - 1);
+    atomicAdd(&hist[last_bucket(sp, np)], 1);
+  }
+  __syncthreads();
+  // Exclusive prefix sum of the 256 bucket counts (four waves).
+  int v = tid < 256 ? hist[tid] : 0, incl = v;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  if (tid < 256 && lane == 63) wave_tot[tid >> 6] = incl;
+  __syncthreads();
+  if (tid < 256) {
+    int before = 0;
+    for (int w = 0; w < (tid >> 6); ++w) before += wave_tot[w];
+    hist[tid] = before + incl - v;                           // bucket start
+    if (tid == 255) *a.n_units = before + incl;
+  }
+  __syncthreads();
+  for (int s = tid; s < a.num_seqs; s += 1024) {
+    const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
+    const int np = sp.nparts > 1 ? sp.nparts : 1;
+    if (np > 1) {
+      const int pos = atomicAdd(&hist[0], np - 1);
+      for (int q = 0; q < np - 1; ++q) a.units[pos + q] = make_int2(s, q);
+    }
+    a.units[atomicAdd(&hist[last_bucket(sp, np)], 1)] = make_int2(s, np - 1);
+  }
+}
+
 struct RArgs {
   void* out;
   const int32_t* lens;
@@ -887,27 +978,70 @@ struct RArgs {
   int part_tokens, max_parts;
 };
 
-// One wave per (sequence, head): merge the partitions in order p = 0, 1, ...
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// One wave per (sequence, head) merges the partitions of a split sequence:
+// with M = max_p m_p, out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
+// Lanes first read the (m, l) pairs of 64 partitions at a time, then every
+// lane accumulates its head-dim elements over the partitions in order
+// p = 0, 1, ..., taking each weight from the lane that computed it.  All
+// sums run in a fixed order, so reruns give identical bits.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_reduce(const RArgs a) {
+  constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.num_seqs * a.num_heads) return;
   const int s = item / a.num_heads;
   const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
   if (sp.bad || sp.nparts <= 1) return;   // written by the partition kernel
+  const int np = sp.nparts;
   const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
-  const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D;
+  const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
+
   float M = kEmptyMax;
-  for (int p = 0; p < sp.nparts; ++p) M = fmaxf(M, ml[p].x);
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
+  M = wave_max(M);
   float lsum = 0.f;
-  for (int p = 0; p < sp.nparts; ++p) lsum += ml[p].y * fast_exp2(ml[p].x - M);
-  const float inv = 1.f / lsum;
-  for (int e = lane; e < D; e += 64) {
-    float asum = 0.f;
-    for (int p = 0; p < sp.nparts; ++p) asum += pacc[(size_t)p * D + e] * fast_exp2(ml[p].x - M);
-    store_elem<DT>(a.out, (size_t)item * D + e, asum * inv);
+  for (int p = lane; p < np; p += 64) lsum += ml[p].y * fast_exp2(ml[p].x - M);
+  const float inv = 1.f / wave_sum(lsum);
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const float wl = p0 + lane < np ? fast_exp2(ml[p0 + lane].x - M) : 0.f;
+    const int cnt = min(64, np - p0);
+    auto add = [&](int j) {
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                    __builtin_bit_cast(int, wl), j));
+      const float* src = pacc + (size_t)(p0 + j) * D;
+      if constexpr (EPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src);
+        acc[0] = fmaf(w, v.x, acc[0]);
+        acc[1] = fmaf(w, v.y, acc[1]);
+      } else {
+        acc[0] = fmaf(w, src[0], acc[0]);
+      }
+    };
+    int j = 0;
+    for (; j + 4 <= cnt; j += 4) {     // four independent loads in flight
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) add(j + jj);
+    }
+    for (; j < cnt; ++j) add(j);
   }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) store_elem<DT>(a.out, (size_t)item * D + lane * EPL + e, acc[e] * inv);
 }
 
 struct CArgs {
@@ -994,17 +1128,21 @@ hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t ld
   return hipGetLastError();
 }
 
+// Waves per workgroup of the matrix-core kernel.  Each wave holds two
+// 16-token K/V slots in LDS (16 KiB at head_dim 128); two workgroups of four
+// waves fill 128 KiB of the 160 KiB of LDS per CU.
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 4
+#endif
+
 template <int DT>
-hipError_t dispatch_mfma(const KArgs& ka, int d, int waves, bool big, bool nt, int grid,
-                         hipStream_t st) {
+hipError_t dispatch_mfma(const KArgs& ka, int d, bool big, bool nt, int grid, hipStream_t st) {
+  constexpr int W = PA_MFMA_WAVES;
   // Two slots of one 16-token K tile and V tile per wave; the merge of the
   // waves after the loop reuses them.
-  const size_t lds = (size_t)waves * 2 * 2 * 16 * d * 2;
-  if (d == 64)
-    return waves >= 8 ? launch_mfma_t<DT, 64, 8>(ka, big, nt, grid, lds, st)
-                      : launch_mfma_t<DT, 64, 4>(ka, big, nt, grid, lds, st);
-  return waves >= 8 ? launch_mfma_t<DT, 128, 8>(ka, big, nt, grid, lds, st)
-                    : launch_mfma_t<DT, 128, 4>(ka, big, nt, grid, lds, st);
+  const size_t lds = (size_t)W * 2 * 2 * 16 * d * 2;
+  if (d == 64) return launch_mfma_t<DT, 64, W>(ka, big, nt, grid, lds, st);
+  return launch_mfma_t<DT, 128, W>(ka, big, nt, grid, lds, st);
 }
 
 template <int DT>
@@ -1016,9 +1154,17 @@ hipError_t launch_reduce_t(const RArgs& ra, int d, int grid, hipStream_t st) {
 
 }  // namespace
 
-size_t splitk_partial_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions) {
+// Split-K workspace: acc [B][Hq][Pmax][D] fp32, (m, l) [B][Hq][Pmax], then
+// the plan: the unit count (padded to 256 bytes) and [B * Pmax] units.
+static size_t plan_offset(int num_seqs, int num_heads, int head_dim, int max_partitions) {
   const size_t slots = (size_t)num_seqs * num_heads * max_partitions;
-  return slots * head_dim * sizeof(float) + slots * sizeof(float2);
+  const size_t b = slots * head_dim * sizeof(float) + slots * sizeof(float2);
+  return (b + 255) / 256 * 256;
+}
+
+size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions) {
+  return plan_offset(num_seqs, num_heads, head_dim, max_partitions) + 256 +
+         (size_t)num_seqs * max_partitions * sizeof(int2);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
@@ -1033,6 +1179,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t slots = (size_t)p.num_seqs * p.num_heads * p.max_partitions;
   ka.ws_acc = p.workspace;
   ka.ws_ml = p.workspace ? reinterpret_cast<float2*>(p.workspace + slots * p.head_dim) : nullptr;
+  int* plan = nullptr;
+  if (p.workspace != nullptr)
+    plan = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(p.workspace) +
+                                  plan_offset(p.num_seqs, p.num_heads, p.head_dim, p.max_partitions));
+  ka.n_units = plan;
+  ka.units = plan ? reinterpret_cast<const int2*>(plan + 64) : nullptr;
   ka.num_seqs = p.num_seqs;
   ka.num_heads = p.num_heads;
   ka.num_kv_heads = p.num_kv_heads;
@@ -1063,10 +1215,23 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
   hipError_t e;
+  if (plan != nullptr) {
+    PArgs pa_;
+    pa_.lens = p.context_lens;
+    pa_.n_units = plan;
+    pa_.units = reinterpret_cast<int2*>(plan + 64);
+    pa_.num_seqs = p.num_seqs;
+    pa_.part_tokens = p.partition_size;
+    pa_.max_parts = p.max_partitions;
+    pa_.max_blocks = p.max_blocks_per_seq;
+    pa_.bs_log2 = ka.bs_log2;
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, pa_);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (mfma) {
-    const int mw = 4;     // 4 waves x 16 KiB of slots = 64 KiB of LDS per workgroup
-    e = p.dtype == kF16 ? dispatch_mfma<kF16>(ka, p.head_dim, mw, big, nt, (int)grid, stream)
-                        : dispatch_mfma<kBF16>(ka, p.head_dim, mw, big, nt, (int)grid, stream);
+    e = p.dtype == kF16 ? dispatch_mfma<kF16>(ka, p.head_dim, big, nt, (int)grid, stream)
+                        : dispatch_mfma<kBF16>(ka, p.head_dim, big, nt, (int)grid, stream);
   } else {
     switch (p.dtype) {
       case kF32: e = dispatch_d<kF32>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;

@@ -52,8 +52,8 @@ struct CacheWriteParams {
   int dtype;
 };
 
-// Byte size of the split-K partials for these sizes (no rounding).
-size_t splitk_partial_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions);
+// Byte size of the split-K workspace for these sizes: partials and plan.
+size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions);
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
 // Single pass when p.workspace == nullptr (then p.max_partitions must be 1).

@@ -80,7 +80,9 @@ def test_cache_write_rejects(lib):
 
 def test_splitk_workspace_sizing_and_rejects(lib):
     need = pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 256)
-    assert need == ((64 * 32 * 8 * (128 + 2) * 4) + 255) // 256 * 256
+    partials = ((64 * 32 * 8 * (128 + 2) * 4) + 255) // 256 * 256
+    plan = 256 + 64 * 8 * 8                  # unit count, then one (seq, part) pair each
+    assert need == (partials + plan + 255) // 256 * 256
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 24) == 0
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 96, 2048, 256) == 0
 
