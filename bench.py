@@ -234,7 +234,9 @@ def main() -> int:
         except Exception:
             traffic = None
 
-    kernel = "k_decode" if entry == "single" else "k_decode (partitions) + k_reduce"
+    mfma = dt != "f32" and w.group_ratio >= 2 and not args.valu_only
+    kname = "k_decode_mfma" if mfma else "k_decode"
+    kernel = kname if entry == "single" else f"k_plan + {kname} (partitions) + k_reduce"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
