@@ -33,8 +33,10 @@ METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and KV tokens/se
 # partitions, the best trade between balance and per-partition overhead for
 # its log-normal length mix (lengths up to 16384).
 DEFAULT_ENTRY = {"llama2_7b": ("single", None), "long_bs512": ("splitk", 512),
-                 "gqa_70b": ("splitk", 4096), "shared_prefix": ("single", None),
+                 "gqa_70b": ("splitk", 4096), "shared_prefix": ("shared", 1024),
                  "tiny": ("single", None)}
+ENTRY_NAME = {"single": "pa_decode", "splitk": "pa_decode_splitk",
+              "shared": "pa_decode_shared_prefix"}
 
 
 def log(*a):
@@ -108,7 +110,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_7b", choices=sorted(WORKLOADS))
-    ap.add_argument("--entry", default=None, choices=["single", "splitk"])
+    ap.add_argument("--entry", default=None, choices=["single", "splitk", "shared"])
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -144,7 +146,7 @@ def main() -> int:
     entry, P = DEFAULT_ENTRY[w.name]
     if args.entry:
         entry = args.entry
-        P = args.partition or (w.partition_size or 256) if entry == "splitk" else None
+        P = args.partition or (w.partition_size or 1024) if entry != "single" else None
     elif args.partition:
         P = args.partition
     t = time.perf_counter()
@@ -180,6 +182,18 @@ def main() -> int:
     if entry == "splitk":
         need = pa.pa_decode_splitk_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, maxlen, P)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if entry == "shared":
+        if case.shared_groups is None:
+            raise SystemExit("--entry shared needs a workload with prompt groups")
+        sg = np.full(w.num_seqs, -1, dtype=np.int32)
+        for gi, members in enumerate(case.shared_groups):
+            sg[members] = gi
+        seq_group = d(sg)
+        group_prefix = d(np.full(len(case.shared_groups), w.prompt_len, dtype=np.int32))
+        max_group = int(case.shared_groups.shape[1])
+        need = pa.pa_decode_shared_prefix_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim,
+                                                          maxlen, P, len(case.shared_groups))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     shared = case.shared_groups is not None or args.cached   # keep K/V loads cached
 
@@ -187,6 +201,10 @@ def main() -> int:
         if entry == "single":
             pa.pa_decode(q, kp, vp, tb, ln, scale=scale, out=out, shared_kv=shared,
                          valu_only=args.valu_only)
+        elif entry == "shared":
+            pa.pa_decode_shared_prefix(q, kp, vp, tb, ln, seq_group, group_prefix, max_group, P,
+                                       maxlen, scale=scale, out=out, workspace=ws,
+                                       shared_kv=shared)
         else:
             pa.pa_decode_splitk(q, kp, vp, tb, ln, partition_size=P, max_context_len=maxlen,
                                 scale=scale, out=out, workspace=ws, shared_kv=shared,
@@ -214,7 +232,10 @@ def main() -> int:
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     e = w.elem_bytes
-    dec_bytes = algorithmic_bytes(case)
+    # With prompt groups the blocks a group shares are counted once (unique
+    # bytes, what HBM must deliver); the per-sequence sum is reported beside.
+    dec_bytes = algorithmic_bytes(case, unique=case.shared_groups is not None)
+    logical_bytes = algorithmic_bytes(case)
     cw_bytes = 4 * w.num_seqs * w.num_kv_heads * w.head_dim * e + 4 * 2 * w.num_seqs
     step_bytes = dec_bytes + cw_bytes
     ms_step = elapsed * 1e3 / K
@@ -234,7 +255,7 @@ def main() -> int:
         except Exception:
             traffic = None
 
-    mfma = dt != "f32" and w.group_ratio >= 2 and not args.valu_only
+    mfma = entry == "shared" or (dt != "f32" and w.group_ratio >= 2 and not args.valu_only)
     kname = "k_decode_mfma" if mfma else "k_decode"
     kernel = kname if entry == "single" else f"k_plan + {kname} (partitions) + k_reduce"
     res = {
@@ -251,7 +272,7 @@ def main() -> int:
         "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[dt],
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "seed": case.seed,
-                   "entry": "pa_decode" if entry == "single" else "pa_decode_splitk",
+                   "entry": ENTRY_NAME[entry],
                    "partition_size": P, "accumulate": "f32", "shared_kv_flag": shared,
                    "valu_only": bool(args.valu_only),
                    "global_batch": w.num_seqs, "kv_tokens": tokens,
@@ -262,7 +283,8 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kernel,
                      "avg_launch_us": round(dec_ms * 1e3, 3),
-                     "algorithmic_bytes_per_launch": dec_bytes},
+                     "algorithmic_bytes_per_launch": dec_bytes,
+                     "logical_bytes_per_launch": logical_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -179,6 +179,51 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
                      void* workspace, size_t workspace_bytes, int flags, void* stream);
 
 /*
+ * Bytes of device workspace pa_decode_shared_prefix needs: the split-K
+ * partials for ceil(max_context_len / partition_size) + 1 partitions per
+ * sequence, the launch plan, and the group tables (about 16 bytes per group
+ * and 4 per sequence).  Returns 0 for invalid sizes.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                               int max_context_len, int partition_size,
+                                               int num_groups);
+
+/*
+ * pa_decode_shared_prefix -- the same result as pa_decode for a batch in
+ * which groups of sequences share the blocks of a common prompt (parallel
+ * sampling, beam candidates): several requests using the same KV blocks is
+ * the block-level sharing of "Efficient Memory Management ... paper summary",
+ * key feature 2 and "Benefits" (less duplication of the KV cache).  Here the
+ * sharing also saves bandwidth: each partition of a group's prompt is read
+ * once, by one workgroup per KV head whose matrix-core columns are the
+ * queries of every member, instead of once per member.
+ *
+ * seq_group[s] is the group of sequence s, or -1 for a sequence that shares
+ * nothing; group_prefix_len[i] is the number of prompt tokens group i shares:
+ * a multiple of block_size, at most every member's length, and the first
+ * group_prefix_len[i] / block_size entries of every member's table name the
+ * same blocks.  Each group has at most max_group_size members.  The member's
+ * own tokens [group_prefix_len, L) and ungrouped sequences are processed per
+ * sequence.  Every sequence is cut into the prompt's partitions and its own
+ * partitions of partition_size tokens, and the partials are merged in fixed
+ * order as in pa_decode_splitk, so results do not depend on scheduling.
+ * A group that breaks the contract gives its members NaN rows.
+ *
+ * fp16 and bf16 only (PA_ERR_UNSUPPORTED otherwise); PA_FLAG_SHARED_KV is
+ * accepted (blocks shared with other calls), PA_FLAG_VALU_ONLY is rejected.
+ * max_context_len, partition_size and the workspace are as for
+ * pa_decode_splitk, with pa_decode_shared_prefix_workspace_bytes(...) bytes.
+ */
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* seq_group, const int32_t* group_prefix_len,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                            int dtype, int num_groups, int max_group_size, int partition_size,
+                            int max_context_len, void* workspace, size_t workspace_bytes,
+                            int flags, void* stream);
+
+/*
  * pa_check_inputs_host -- validate HOST copies of the device data against the
  * contract above: 0 <= L <= max_blocks_per_seq * block_size, every table entry
  * in use in [0, num_blocks), and, if check_write_targets is nonzero, that no

@@ -34,6 +34,10 @@ _SIGNATURES = {
                           _c_void_p]),
     "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
                              [ctypes.POINTER(_c_int)]),
+    "pa_decode_shared_prefix_workspace_bytes": (_c_size_t, [_c_int] * 6),
+    "pa_decode_shared_prefix": (_c_int, [_c_void_p] * 8 + [_c_int] * 7 +
+                                [_c_float] + [_c_int] * 5 + [_c_void_p, _c_size_t, _c_int,
+                                                              _c_void_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -208,6 +212,46 @@ def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                                  int(max_context_len), workspace.data_ptr(), ws_bytes,
                                  _flags(shared_kv, valu_only), _stream(q.device, stream))
     _check(st, "pa_decode_splitk")
+    return out
+
+
+def pa_decode_shared_prefix_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
+                                            max_context_len: int, partition_size: int,
+                                            num_groups: int) -> int:
+    return int(load().pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_heads, head_dim, max_context_len, partition_size, num_groups))
+
+
+def pa_decode_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor,
+                            seq_group: torch.Tensor, group_prefix_len: torch.Tensor,
+                            max_group_size: int, partition_size: int, max_context_len: int,
+                            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, shared_kv: bool = False,
+                            stream=None) -> torch.Tensor:
+    """Decode for groups of sequences sharing a prompt's blocks; see
+    pa_decode_shared_prefix in include/pa.h.  ``seq_group`` [num_seqs] int32
+    (-1: no group), ``group_prefix_len`` [num_groups] int32."""
+    out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
+                                                           context_lens, scale, out)
+    _dev(seq_group, "seq_group", torch.int32)
+    _dev(group_prefix_len, "group_prefix_len", torch.int32)
+    if seq_group.shape != (B,) or group_prefix_len.dim() != 1:
+        raise ValueError("seq_group must be [num_seqs] and group_prefix_len [num_groups]")
+    G = group_prefix_len.shape[0]
+    need = pa_decode_shared_prefix_workspace_bytes(B, Hq, d, max_context_len, partition_size, G)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pa_decode_shared_prefix(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), seq_group.data_ptr(),
+        group_prefix_len.data_ptr() if G else None, B, Hq, Hkv, d, bs, MB, NB, scale,
+        _DTYPES.get(q.dtype, -1), G, int(max_group_size), int(partition_size),
+        int(max_context_len), workspace.data_ptr(), ws_bytes,
+        PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
+    _check(st, "pa_decode_shared_prefix")
     return out
 
 

@@ -102,6 +102,10 @@ pa::DecodeParams make_params(void* out, const void* q, const void* k_pool, const
   p.partition_size = 0;
   p.max_partitions = 1;
   p.flags = flags;
+  p.seq_group = nullptr;
+  p.group_prefix = nullptr;
+  p.num_groups = 0;
+  p.max_group_size = 1;
   return p;
 }
 
@@ -186,8 +190,76 @@ size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_di
       max_context_len < 0 || partition_size <= 0 || partition_size % 16 != 0)
     return 0;
   const int parts = (int)ceil_div64(max_context_len, partition_size);
-  const size_t bytes = pa::splitk_workspace_bytes(num_seqs, num_heads, head_dim, parts > 0 ? parts : 1);
+  const size_t bytes =
+      pa::splitk_workspace_bytes(num_seqs, num_heads, head_dim, parts > 0 ? parts : 1, 0);
   return (bytes + 255) / 256 * 256;
+}
+
+// A shared prompt can split one partition of a sequence in two (prompt tail
+// and own head), hence one partition more than the plain split.
+static int shared_parts(int max_context_len, int partition_size) {
+  return (int)ceil_div64(max_context_len, partition_size) + 1;
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int head_dim,
+                                               int max_context_len, int partition_size,
+                                               int num_groups) {
+  if (num_seqs < 0 || num_heads <= 0 || (head_dim != 64 && head_dim != 128) ||
+      max_context_len < 0 || partition_size <= 0 || partition_size % 16 != 0 || num_groups < 0)
+    return 0;
+  const size_t bytes = pa::splitk_workspace_bytes(
+      num_seqs, num_heads, head_dim, shared_parts(max_context_len, partition_size), num_groups);
+  return (bytes + 255) / 256 * 256;
+}
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* seq_group, const int32_t* group_prefix_len,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                            int dtype, int num_groups, int max_group_size, int partition_size,
+                            int max_context_len, void* workspace, size_t workspace_bytes,
+                            int flags, void* stream) {
+  int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                        dtype, flags);
+  if (st) return st;
+  if (dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "shared-prefix decode runs on the matrix cores: fp16 or bf16");
+  if (flags & PA_FLAG_VALU_ONLY)
+    return fail(PA_ERR_INVALID_ARG, "PA_FLAG_VALU_ONLY does not apply to shared-prefix decode");
+  if (partition_size <= 0 || partition_size % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be a positive multiple of 16 (got %d)",
+                partition_size);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARG,
+                "max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (num_groups < 0) return fail(PA_ERR_INVALID_ARG, "num_groups must be >= 0 (got %d)", num_groups);
+  if (max_group_size < 1 || max_group_size > num_seqs + (num_seqs == 0))
+    return fail(PA_ERR_INVALID_ARG, "max_group_size %d outside [1, num_seqs]", max_group_size);
+  if ((int64_t)max_group_size * (num_heads / num_kv_heads) > 4096)
+    return fail(PA_ERR_INVALID_ARG, "max_group_size * query heads per KV head exceeds 4096");
+  if (num_seqs == 0) return ok();
+  if (!seq_group || (num_groups > 0 && !group_prefix_len))
+    return fail(PA_ERR_NULL, "seq_group and group_prefix_len are required");
+  const size_t need = pa_decode_shared_prefix_workspace_bytes(
+      num_seqs, num_heads, head_dim, max_context_len, partition_size, num_groups);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                                   num_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, num_blocks, scale, dtype, flags);
+  p.partition_size = partition_size;
+  p.max_partitions = shared_parts(max_context_len, partition_size);
+  p.workspace = static_cast<float*>(workspace);
+  p.seq_group = seq_group;
+  p.group_prefix = group_prefix_len;
+  p.num_groups = num_groups;
+  p.max_group_size = max_group_size;
+  return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
 int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -206,6 +206,14 @@ struct KArgs {
   float2* ws_ml;        // [B][Hq][max_parts] of (max, sum)
   const int* n_units;   // split-K plan: number of (sequence, partition) units
   const int2* units;    // split-K plan: units, longest first
+  // Shared-prompt decode (nullptr otherwise): the group of each sequence
+  // (-1: none), each group's shared prompt length, and the members of each
+  // group (members[group_start[i] .. group_start[i+1]) ).
+  const int32_t* seq_group;
+  const int32_t* group_prefix;
+  const int* group_start;
+  const int* members;
+  int num_groups;
   int num_seqs, num_heads, num_kv_heads, bs_log2, max_blocks, num_blocks;
   int group;            // query heads per KV head
   int chunks;           // group / GW
@@ -213,6 +221,114 @@ struct KArgs {
   int max_parts;
   float scale_log2;     // scale * log2(e)
 };
+
+// Partition layout of one sequence.  Without a prompt group, tokens [0, L)
+// are cut into partitions of P tokens.  A sequence whose group shares a
+// prompt of Lp tokens (a multiple of the block size, the same blocks at the
+// head of every member's table) has the prompt's partitions first -- they
+// are computed once for the whole group -- then its own tokens [Lp, L) in
+// partitions of P.  Out-of-contract sequences get no partitions and a NaN
+// output row.
+struct SeqLayout {
+  int len, lp, np_pre, nparts;
+  bool bad;
+};
+__device__ __forceinline__ SeqLayout seq_layout(const KArgs& a, int s) {
+  SeqLayout r;
+  r.len = a.lens[s];
+  r.lp = 0;
+  bool bad = r.len < 0 || r.len > (a.max_blocks << a.bs_log2);
+  if (a.seq_group != nullptr) {
+    const int gi = a.seq_group[s];
+    if (gi >= a.num_groups || gi < -1) bad = true;
+    else if (gi >= 0) r.lp = a.group_prefix[gi];
+    if (r.lp < 0 || r.lp > r.len || (r.lp & ((1 << a.bs_log2) - 1)) != 0) bad = true;
+  }
+  if (bad) { r.len = 0; r.lp = 0; }
+  r.np_pre = (r.lp + a.part_tokens - 1) / a.part_tokens;
+  r.nparts = r.np_pre + (r.len - r.lp + a.part_tokens - 1) / a.part_tokens;
+  if (r.nparts > a.max_parts) { bad = true; r.len = r.lp = r.np_pre = r.nparts = 0; }
+  r.bad = bad;
+  return r;
+}
+
+// One query column of a matrix-core workgroup: whose query it is, which
+// partition slot of that sequence it fills, and whether it writes the output
+// directly (the sequence has a single partition).
+struct Col {
+  int seq, head, part;
+  bool valid, direct, bad;
+};
+
+// The unit a matrix-core workgroup works on: KV head, chunk of 16 query
+// columns, the sequence whose table supplies the blocks, and the token range.
+// A prompt unit (prompt_group >= 0) covers one partition of a group's shared
+// prompt for all members at once: column c is member c / G, query head
+// g*G + c % G.  Otherwise the columns are query heads of one sequence.
+struct KUnit {
+  int ch, g, ts, t_begin, t_end, prompt_group, s, p, ncols;
+  bool bad;
+};
+__device__ __forceinline__ bool resolve_kunit(const KArgs& a, KUnit& u, SeqLayout& lay) {
+  int wg = blockIdx.x;
+  u.ch = wg % a.chunks;  wg /= a.chunks;
+  u.g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
+  int x = wg, y = 0;
+  if (a.units != nullptr) {
+    if (wg >= *a.n_units) return false;
+    const int2 v = a.units[wg];
+    x = v.x;
+    y = v.y;
+  }
+  u.bad = false;
+  if (x < 0) {
+    const int gi = -x - 1;
+    const int first = a.group_start[gi], cnt = a.group_start[gi + 1] - first;
+    const int lp = a.group_prefix[gi];
+    u.prompt_group = gi;
+    u.ts = a.members[first];
+    u.s = -1;
+    u.p = y;
+    u.t_begin = y * a.part_tokens;
+    u.t_end = min(u.t_begin + a.part_tokens, lp);
+    u.ncols = min(16, cnt * a.group - u.ch * 16);
+  } else {
+    lay = seq_layout(a, x);
+    u.prompt_group = -1;
+    u.ts = u.s = x;
+    u.p = y;
+    u.bad = lay.bad;
+    u.t_begin = lay.lp + (y - lay.np_pre) * a.part_tokens;
+    u.t_end = min(u.t_begin + a.part_tokens, lay.len);
+    if (lay.nparts == 0) u.t_begin = u.t_end = 0;
+    u.ncols = min(16, a.group - u.ch * 16);
+  }
+  return u.ncols > 0;
+}
+__device__ __forceinline__ Col column_of(const KArgs& a, const KUnit& u, const SeqLayout& lay, int n) {
+  Col c;
+  const int cc = u.ch * 16 + n;
+  c.part = u.p;
+  if (u.prompt_group >= 0) {
+    const int first = a.group_start[u.prompt_group];
+    const int cnt = a.group_start[u.prompt_group + 1] - first;
+    const int mi = cc / a.group;
+    c.valid = n < u.ncols && mi < cnt;
+    c.seq = c.valid ? a.members[first + mi] : 0;
+    c.head = u.g * a.group + cc % a.group;
+    const SeqLayout ml = seq_layout(a, c.seq);
+    c.bad = ml.bad;
+    c.valid = c.valid && !ml.bad;      // an out-of-contract member writes its NaN row itself
+    c.direct = ml.nparts == 1;
+  } else {
+    c.valid = n < u.ncols;
+    c.seq = u.s;
+    c.head = u.g * a.group + cc;
+    c.bad = lay.bad;
+    c.direct = lay.nparts <= 1;
+  }
+  return c;
+}
 
 // The (KV head, head chunk, sequence, partition) a workgroup works on.
 // Split-K launches follow the plan written by k_plan: workgroup index
@@ -695,17 +811,14 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
   const int qa = lane & 3;            // position in the quad
   const int qb = (lane >> 2) & 3;     // quad index inside the lane group
 
-  Unit un;
-  if (!resolve_unit(a, un)) return;
-  const int ch = un.ch, g = un.g, s = un.s, p = un.p;
-  const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
-  const bool direct = sp.nparts <= 1;    // the only partition writes the output itself
-  const int t_begin = p * a.part_tokens;
-  const int t_end = min(t_begin + a.part_tokens, sp.len);
+  KUnit un;
+  SeqLayout lay;
+  if (!resolve_kunit(a, un, lay)) return;
+  const int g = un.g;
+  const int t_begin = un.t_begin, t_end = un.t_end;
   const int nsteps = t_end > t_begin ? (t_end - t_begin + 15) >> 4 : 0;
-
-  const int h0 = g * a.group + ch * 16;
-  const int nh = min(16, a.group - ch * 16);     // real heads in this chunk
+  const int nh = un.ncols;                       // columns in use in this chunk
+  const Col col = column_of(a, un, lay, n);      // this lane's column
   uint4 qv[NI];                                  // Q^T operand, loaded below
 
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
@@ -721,7 +834,7 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
   const int bs_mask = (1 << a.bs_log2) - 1;
   const size_t tile_bytes = (size_t)ROWB << a.bs_log2;
   const size_t block_bytes = tile_bytes * a.num_kv_heads;
-  const const_i32_ptr trow = (const_i32_ptr)(a.tables + (size_t)s * a.max_blocks);
+  const const_i32_ptr trow = (const_i32_ptr)(a.tables + (size_t)un.ts * a.max_blocks);
   bool bad_block = false;
 
   const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
@@ -815,17 +928,17 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
     }
   };
 
-  // Q^T operand: head h0+n, chunk 4i + lg of its row (zero beyond the
-  // group).  Its loads go out between the first and second slot's K/V loads,
+  // Q^T operand: column n's query row, chunk 4i + lg (zero for unused
+  // columns).  Its loads go out between the first and second slot's K/V loads,
   // so their latency overlaps the first tile's and waiting for them (vmcnt
   // counts in order) leaves the second slot in flight.
   auto load_q = [&]() {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       qv[i] = make_uint4(0, 0, 0, 0);
-      if (n < nh)
+      if (col.valid)
         qv[i] = *reinterpret_cast<const uint4*>(
-            a.q + ((size_t)(s * a.num_heads + h0 + n) * D) * EB + (4 * i + lg) * 16);
+            a.q + ((size_t)(col.seq * a.num_heads + col.head) * D) * EB + (4 * i + lg) * 16);
     }
   };
 
@@ -869,7 +982,14 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
   float* s_m = s_acc + (size_t)W * nh * D;                // [W][16]
   float* s_l = s_m + W * 16;                              // [W][16]
   int* s_bad = reinterpret_cast<int*>(s_l + W * 16);
+  int* s_col = s_bad + 1;                                 // [16][4]: seq, head, part, flags
   if (threadIdx.x == 0) *s_bad = 0;
+  if (threadIdx.x < 16) {
+    s_col[4 * n] = col.seq;
+    s_col[4 * n + 1] = col.head;
+    s_col[4 * n + 2] = col.part;
+    s_col[4 * n + 3] = (col.valid ? 1 : 0) | (col.direct ? 2 : 0) | (col.bad ? 4 : 0);
+  }
   __syncthreads();
   if (bad_block) *s_bad = 1;
   if (n < nh) {
@@ -883,9 +1003,13 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
     if (lg == 0) { s_m[wave * 16 + n] = m; s_l[wave * 16 + n] = lsum; }
   }
   __syncthreads();
-  const bool poisoned = sp.bad || *s_bad;
+  const bool unit_bad = un.bad || *s_bad;
   for (int idx = threadIdx.x; idx < nh * D; idx += W * 64) {
     const int hh = idx / D, e = idx % D;
+    const int cflags = s_col[4 * hh + 3];
+    if (!(cflags & 1)) continue;
+    const int cseq = s_col[4 * hh], chead = s_col[4 * hh + 1], cpart = s_col[4 * hh + 2];
+    const bool poisoned = unit_bad || (cflags & 4);
     float M = s_m[hh];
 #pragma unroll
     for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w * 16 + hh]);
@@ -896,13 +1020,12 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
       ls += s_l[w * 16 + hh] * f;
       as += s_acc[((size_t)w * nh + hh) * D + e] * f;
     }
-    const int h = h0 + hh;
-    if (direct) {
+    if (cflags & 2) {
       float v = ls > 0.f ? as / ls : 0.f;
       if (poisoned) v = __builtin_nanf("");
-      store_elem<DT>(a.out, (size_t)(s * a.num_heads + h) * D + e, v);
+      store_elem<DT>(a.out, (size_t)(cseq * a.num_heads + chead) * D + e, v);
     } else {
-      const size_t slot = (size_t)(s * a.num_heads + h) * a.max_parts + p;
+      const size_t slot = (size_t)(cseq * a.num_heads + chead) * a.max_parts + cpart;
       if (poisoned) { as = __builtin_nanf(""); ls = __builtin_nanf(""); }
       a.ws_acc[slot * D + e] = as;
       if (e == 0) a.ws_ml[slot] = make_float2(M, ls);
@@ -911,72 +1034,133 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
 }
 
 struct PArgs {
-  const int32_t* lens;
+  KArgs k;              // sizes, lengths and (shared-prompt decode) the caller's groups
   int* n_units;
-  int2* units;          // [num_seqs * max_parts]
-  int num_seqs, part_tokens, max_parts, max_blocks, bs_log2;
+  int2* units;          // [(num_groups + num_seqs) * max_parts]
+  int* group_fill;      // [num_groups] scratch
+  int* group_start;     // [num_groups + 1]
+  int* members;         // [num_seqs]
+  int* group_lp;        // [num_groups] prompt lengths the other launches use
+  int max_group_size;
 };
 
-// Split-K plan: every sequence contributes ceil(L/P) units (sequence,
-// partition), at least one.  All but the last are full (P tokens); the last
-// holds the remainder.  One workgroup counting-sorts the units by size into
-// 256 buckets, largest first, so the partition kernel's workgroups are
-// dispatched longest first.  The order inside a bucket depends on timing,
-// but no result does: each unit's arithmetic and the reduce are fixed.
-__global__ __launch_bounds__(1024) void k_plan(const PArgs a) {
-  __shared__ int hist[256];
-  __shared__ int wave_tot[4];
-  const int tid = threadIdx.x;
-  if (tid < 256) hist[tid] = 0;
-  __syncthreads();
-  auto last_bucket = [&](const SeqParts& sp, int np) {
-    const int size = sp.len - (np - 1) * a.part_tokens;     // 0 for an empty sequence
-    const long long b = ((long long)(a.part_tokens - size) * 256) / a.part_tokens;
-    return (int)(b > 255 ? 255 : b);
-  };
-  for (int s = tid; s < a.num_seqs; s += 1024) {
-    const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
-    const int np = sp.nparts > 1 ? sp.nparts : 1;
-    if (np > 1) atomicAdd(&hist[0], np - 1);
-    atomicAdd(&hist[last_bucket(sp, np)], 1);
-  }
-  __syncthreads();
-  // Exclusive prefix sum of the 256 bucket counts (four waves).
-  int v = tid < 256 ? hist[tid] : 0, incl = v;
-  const int lane = tid & 63;
+// Exclusive prefix sum of n ints (src -> dst, dst[n] = total) by one
+// workgroup of 1024 threads, 1024 entries at a time.
+__device__ __forceinline__ void block_exclusive_scan(const int* src, int* dst, int n, int* s_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int v = base + tid < n ? src[base + tid] : 0;
+    int incl = v;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  if (tid < 256 && lane == 63) wave_tot[tid >> 6] = incl;
-  __syncthreads();
-  if (tid < 256) {
-    int before = 0;
-    for (int w = 0; w < (tid >> 6); ++w) before += wave_tot[w];
-    hist[tid] = before + incl - v;                           // bucket start
-    if (tid == 255) *a.n_units = before + incl;
-  }
-  __syncthreads();
-  for (int s = tid; s < a.num_seqs; s += 1024) {
-    const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
-    const int np = sp.nparts > 1 ? sp.nparts : 1;
-    if (np > 1) {
-      const int pos = atomicAdd(&hist[0], np - 1);
-      for (int q = 0; q < np - 1; ++q) a.units[pos + q] = make_int2(s, q);
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
     }
-    a.units[atomicAdd(&hist[last_bucket(sp, np)], 1)] = make_int2(s, np - 1);
+    if (lane == 63) s_tot[wv] = incl;
+    __syncthreads();
+    int before = carry;
+    for (int w = 0; w < wv; ++w) before += s_tot[w];
+    if (base + tid < n) dst[base + tid] = before + incl - v;
+    int chunk = 0;
+    for (int w = 0; w < 16; ++w) chunk += s_tot[w];
+    __syncthreads();
+    carry += chunk;
   }
+  if (tid == 0) dst[n] = carry;
 }
 
-struct RArgs {
-  void* out;
-  const int32_t* lens;
-  const float* ws_acc;
-  const float2* ws_ml;
-  int num_seqs, num_heads, max_blocks, bs_log2;
-  int part_tokens, max_parts;
-};
+// Split-K plan, one workgroup.  Every sequence contributes its own
+// partitions (at least one unit, so that empty or out-of-contract sequences
+// still write their row); with shared prompts every group also contributes
+// the partitions of its prompt, each a single unit for all members.  The
+// units are counting-sorted by size into 256 buckets, largest first, so the
+// partition kernel's workgroups are dispatched longest first (longest-first
+// list scheduling).  The order inside a bucket and the order of a group's
+// members depend on timing; no result does, because every column's
+// arithmetic and the reduce's order are fixed.
+__global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
+  __shared__ int hist[257];           // bucket counts, then starts (+ total)
+  __shared__ int s_tot[16];
+  const int tid = threadIdx.x;
+  const int P = pa.k.part_tokens;
+  const bool shared = pa.k.seq_group != nullptr;
+  const int NG = shared ? pa.k.num_groups : 0;
+  if (tid < 256) hist[tid] = 0;
+  for (int i = tid; i < NG; i += 1024) pa.group_fill[i] = 0;
+  __syncthreads();
+  KArgs a = pa.k;
+  if (shared) {
+    // Members of each group, grouped by a counting sort.
+    for (int s = tid; s < a.num_seqs; s += 1024) {
+      const int gi = a.seq_group[s];
+      if (gi >= 0 && gi < NG) atomicAdd(&pa.group_fill[gi], 1);
+    }
+    __syncthreads();
+    block_exclusive_scan(pa.group_fill, pa.group_start, NG, s_tot);
+    __syncthreads();
+    for (int i = tid; i < NG; i += 1024) {
+      // A prompt that is not whole blocks, longer than a table can hold, cut
+      // into more partitions than a sequence may have, or shared by more
+      // members than the launch's column chunks cover is out of contract:
+      // it is marked invalid (-1), so its members get NaN rows.
+      const int cnt = pa.group_fill[i];
+      const int lp = a.group_prefix[i];
+      const bool ok = cnt <= pa.max_group_size && lp >= 0 &&
+                      lp <= (a.max_blocks << a.bs_log2) &&
+                      (lp & ((1 << a.bs_log2) - 1)) == 0 && (lp + P - 1) / P <= a.max_parts;
+      pa.group_lp[i] = ok ? lp : -1;
+      pa.group_fill[i] = 0;
+    }
+    __syncthreads();
+    for (int s = tid; s < a.num_seqs; s += 1024) {
+      const int gi = a.seq_group[s];
+      if (gi >= 0 && gi < NG) pa.members[pa.group_start[gi] + atomicAdd(&pa.group_fill[gi], 1)] = s;
+    }
+    __syncthreads();
+    a.group_prefix = pa.group_lp;
+    a.group_start = pa.group_start;
+    a.members = pa.members;
+  }
+  auto bucket = [&](int size) {
+    const long long b = ((long long)(P - size) * 256) / P;
+    return (int)(b > 255 ? 255 : b);
+  };
+  // Prompt partitions of a group: np_pre units, the last holding the rest.
+  auto prompt_parts = [&](int gi) {
+    const int cnt = pa.group_start[gi + 1] - pa.group_start[gi];
+    const int lp = a.group_prefix[gi];
+    if (cnt == 0 || lp <= 0) return 0;
+    return (lp + P - 1) / P;
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    // pass 0 counts units per size bucket, pass 1 places them
+    auto put = [&](int size, int x, int y) {
+      const int b = bucket(size);
+      if (pass == 0) atomicAdd(&hist[b], 1);
+      else pa.units[atomicAdd(&hist[b], 1)] = make_int2(x, y);
+    };
+    for (int gi = tid; gi < NG; gi += 1024) {
+      const int np = prompt_parts(gi);
+      for (int q = 0; q < np; ++q) put(min(P, a.group_prefix[gi] - q * P), -(gi + 1), q);
+    }
+    for (int s = tid; s < a.num_seqs; s += 1024) {
+      const SeqLayout lay = seq_layout(a, s);
+      const int own = lay.nparts - lay.np_pre;
+      if (lay.nparts == 0) put(0, s, 0);
+      for (int q = 0; q < own; ++q)
+        put(min(P, lay.len - lay.lp - q * P), s, lay.np_pre + q);
+    }
+    __syncthreads();
+    if (pass == 0) {
+      // bucket counts -> bucket starts; hist[256] = number of units
+      block_exclusive_scan(hist, hist, 256, s_tot);
+      __syncthreads();
+      if (tid == 0) *pa.n_units = hist[256];
+      __syncthreads();
+    }
+  }
+}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -996,15 +1180,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 // p = 0, 1, ..., taking each weight from the lane that computed it.  All
 // sums run in a fixed order, so reruns give identical bits.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void k_reduce(const RArgs a) {
+__global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
   constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.num_seqs * a.num_heads) return;
   const int s = item / a.num_heads;
-  const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
-  if (sp.bad || sp.nparts <= 1) return;   // written by the partition kernel
-  const int np = sp.nparts;
+  const SeqLayout lay = seq_layout(a, s);
+  if (lay.bad || lay.nparts <= 1) return;   // written by the partition kernel
+  const int np = lay.nparts;
   const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
   const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
 
@@ -1128,6 +1312,11 @@ hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t ld
   return hipGetLastError();
 }
 
+// Smallest query-head group sent to the matrix-core kernel.
+#ifndef PA_MFMA_MIN_GROUP
+#define PA_MFMA_MIN_GROUP 2
+#endif
+
 // Waves per workgroup of the matrix-core kernel.  Each wave holds two
 // 16-token K/V slots in LDS (16 KiB at head_dim 128); two workgroups of four
 // waves fill 128 KiB of the 160 KiB of LDS per CU.
@@ -1146,29 +1335,47 @@ hipError_t dispatch_mfma(const KArgs& ka, int d, bool big, bool nt, int grid, hi
 }
 
 template <int DT>
-hipError_t launch_reduce_t(const RArgs& ra, int d, int grid, hipStream_t st) {
-  if (d == 64) hipLaunchKernelGGL((k_reduce<DT, 64>), dim3(grid), dim3(256), 0, st, ra);
-  else hipLaunchKernelGGL((k_reduce<DT, 128>), dim3(grid), dim3(256), 0, st, ra);
+hipError_t launch_reduce_t(const KArgs& ka, int d, int grid, hipStream_t st) {
+  if (d == 64) hipLaunchKernelGGL((k_reduce<DT, 64>), dim3(grid), dim3(256), 0, st, ka);
+  else hipLaunchKernelGGL((k_reduce<DT, 128>), dim3(grid), dim3(256), 0, st, ka);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Split-K workspace: acc [B][Hq][Pmax][D] fp32, (m, l) [B][Hq][Pmax], then
-// the plan: the unit count (padded to 256 bytes) and [B * Pmax] units.
-static size_t plan_offset(int num_seqs, int num_heads, int head_dim, int max_partitions) {
+// Split-K workspace, each part starting on a 256-byte boundary:
+//   acc   [B][Hq][Pmax][D] fp32 and (m, l) [B][Hq][Pmax]
+//   plan  unit count (256 bytes), units [(G + B) * Pmax] of (x, y)
+//   with prompt groups: group_fill [G], group_start [G + 1], members [B],
+//   group_lp [G].
+struct WsLayout {
+  size_t ml, n_units, units, group_fill, group_start, members, group_lp, total;
+};
+static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+static WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_partitions,
+                          int num_groups) {
+  WsLayout w;
   const size_t slots = (size_t)num_seqs * num_heads * max_partitions;
-  const size_t b = slots * head_dim * sizeof(float) + slots * sizeof(float2);
-  return (b + 255) / 256 * 256;
+  w.ml = slots * head_dim * sizeof(float);
+  w.n_units = up256(w.ml + slots * sizeof(float2));
+  w.units = w.n_units + 256;
+  w.group_fill = up256(w.units + (size_t)(num_groups + num_seqs) * max_partitions * sizeof(int2));
+  w.group_start = up256(w.group_fill + (size_t)num_groups * sizeof(int));
+  w.members = up256(w.group_start + (size_t)(num_groups + 1) * sizeof(int));
+  w.group_lp = up256(w.members + (size_t)num_seqs * sizeof(int));
+  w.total = up256(w.group_lp + (size_t)num_groups * sizeof(int));
+  if (num_groups == 0) w.total = w.group_fill;
+  return w;
 }
 
-size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions) {
-  return plan_offset(num_seqs, num_heads, head_dim, max_partitions) + 256 +
-         (size_t)num_seqs * max_partitions * sizeof(int2);
+size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions,
+                              int num_groups) {
+  return ws_layout(num_seqs, num_heads, head_dim, max_partitions, num_groups).total;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
+  const bool shared = p.seq_group != nullptr;
   KArgs ka;
   ka.out = p.out;
   ka.q = static_cast<const uint8_t*>(p.q);
@@ -1176,15 +1383,19 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.v_pool = static_cast<const uint8_t*>(p.v_pool);
   ka.tables = p.block_tables;
   ka.lens = p.context_lens;
-  const size_t slots = (size_t)p.num_seqs * p.num_heads * p.max_partitions;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
+  const WsLayout wl = ws_layout(p.num_seqs, p.num_heads, p.head_dim, p.max_partitions,
+                                shared ? p.num_groups : 0);
   ka.ws_acc = p.workspace;
-  ka.ws_ml = p.workspace ? reinterpret_cast<float2*>(p.workspace + slots * p.head_dim) : nullptr;
-  int* plan = nullptr;
-  if (p.workspace != nullptr)
-    plan = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(p.workspace) +
-                                  plan_offset(p.num_seqs, p.num_heads, p.head_dim, p.max_partitions));
-  ka.n_units = plan;
-  ka.units = plan ? reinterpret_cast<const int2*>(plan + 64) : nullptr;
+  ka.ws_ml = ws ? reinterpret_cast<float2*>(ws + wl.ml) : nullptr;
+  ka.n_units = ws ? reinterpret_cast<const int*>(ws + wl.n_units) : nullptr;
+  ka.units = ws ? reinterpret_cast<const int2*>(ws + wl.units) : nullptr;
+  // The partition and reduce launches read the plan's copies of the groups.
+  ka.seq_group = shared ? p.seq_group : nullptr;
+  ka.group_prefix = shared ? reinterpret_cast<const int32_t*>(ws + wl.group_lp) : nullptr;
+  ka.group_start = shared ? reinterpret_cast<const int*>(ws + wl.group_start) : nullptr;
+  ka.members = shared ? reinterpret_cast<const int*>(ws + wl.members) : nullptr;
+  ka.num_groups = shared ? p.num_groups : 0;
   ka.num_seqs = p.num_seqs;
   ka.num_heads = p.num_heads;
   ka.num_kv_heads = p.num_kv_heads;
@@ -1193,11 +1404,15 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.num_blocks = p.num_blocks;
   ka.group = p.num_heads / p.num_kv_heads;
   // Grouped heads in 16-bit types run on the matrix cores (chunks of up to 16
-  // query heads per workgroup); fp32, single heads, or the VALU-only flag use
-  // the vector path (chunks of GW heads).
-  const bool mfma = p.dtype != kF32 && ka.group >= 2 && !(p.flags & kFlagValuOnly);
+  // query columns per workgroup); fp32, single heads, or the VALU-only flag
+  // use the vector path (chunks of GW heads).  Shared-prompt decode always
+  // runs on the matrix cores: a prompt unit's columns are the queries of all
+  // members of a group.
+  const bool mfma = shared || (p.dtype != kF32 && ka.group >= PA_MFMA_MIN_GROUP &&
+                               !(p.flags & kFlagValuOnly));
   const int gw = ka.group % 4 == 0 ? 4 : (ka.group % 2 == 0 ? 2 : 1);
-  ka.chunks = mfma ? (ka.group + 15) / 16 : ka.group / gw;
+  const int cols = shared ? ka.group * (p.max_group_size > 1 ? p.max_group_size : 1) : ka.group;
+  ka.chunks = mfma ? (cols + 15) / 16 : ka.group / gw;
   ka.part_tokens = p.partition_size;
   ka.max_parts = p.max_partitions;
   ka.scale_log2 = p.scale * kLog2e;
@@ -1211,20 +1426,24 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int row_bytes = p.head_dim * (p.dtype == kF32 ? 4 : 2);
   if (p.workspace == nullptr) waves = gw == 1 && row_bytes <= 256 ? 16 : 8;
   else waves = p.partition_size >= 512 ? 8 : 4;
-  const long long grid = (long long)ka.chunks * p.num_kv_heads * p.num_seqs * p.max_partitions;
+  const long long units = p.workspace == nullptr
+                              ? p.num_seqs
+                              : (long long)(p.num_seqs + (shared ? p.num_groups : 0)) * p.max_partitions;
+  const long long grid = (long long)ka.chunks * p.num_kv_heads * units;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 
   hipError_t e;
-  if (plan != nullptr) {
+  if (ws != nullptr) {
     PArgs pa_;
-    pa_.lens = p.context_lens;
-    pa_.n_units = plan;
-    pa_.units = reinterpret_cast<int2*>(plan + 64);
-    pa_.num_seqs = p.num_seqs;
-    pa_.part_tokens = p.partition_size;
-    pa_.max_parts = p.max_partitions;
-    pa_.max_blocks = p.max_blocks_per_seq;
-    pa_.bs_log2 = ka.bs_log2;
+    pa_.k = ka;
+    pa_.k.group_prefix = p.group_prefix;       // the caller's prompt lengths
+    pa_.n_units = reinterpret_cast<int*>(ws + wl.n_units);
+    pa_.units = reinterpret_cast<int2*>(ws + wl.units);
+    pa_.group_fill = shared ? reinterpret_cast<int*>(ws + wl.group_fill) : nullptr;
+    pa_.group_start = shared ? reinterpret_cast<int*>(ws + wl.group_start) : nullptr;
+    pa_.members = shared ? reinterpret_cast<int*>(ws + wl.members) : nullptr;
+    pa_.group_lp = shared ? reinterpret_cast<int*>(ws + wl.group_lp) : nullptr;
+    pa_.max_group_size = p.max_group_size;
     hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, pa_);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1239,24 +1458,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
       default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;
     }
   }
-  if (e != hipSuccess || p.workspace == nullptr) return e;
-
-  RArgs ra;
-  ra.out = p.out;
-  ra.lens = p.context_lens;
-  ra.ws_acc = ka.ws_acc;
-  ra.ws_ml = ka.ws_ml;
-  ra.num_seqs = p.num_seqs;
-  ra.num_heads = p.num_heads;
-  ra.max_blocks = p.max_blocks_per_seq;
-  ra.bs_log2 = ka.bs_log2;
-  ra.part_tokens = p.partition_size;
-  ra.max_parts = p.max_partitions;
+  if (e != hipSuccess || ws == nullptr) return e;
   const int rgrid = (p.num_seqs * p.num_heads + 3) / 4;
   switch (p.dtype) {
-    case kF32: return launch_reduce_t<kF32>(ra, p.head_dim, rgrid, stream);
-    case kF16: return launch_reduce_t<kF16>(ra, p.head_dim, rgrid, stream);
-    default: return launch_reduce_t<kBF16>(ra, p.head_dim, rgrid, stream);
+    case kF32: return launch_reduce_t<kF32>(ka, p.head_dim, rgrid, stream);
+    case kF16: return launch_reduce_t<kF16>(ka, p.head_dim, rgrid, stream);
+    default: return launch_reduce_t<kBF16>(ka, p.head_dim, rgrid, stream);
   }
 }
 

@@ -34,6 +34,11 @@ struct DecodeParams {
   int partition_size;      // tokens per partition (multiple of 16)
   int max_partitions;      // partitions per sequence covered by the grid
   int flags;               // PA_FLAG_* bits
+  // Shared-prompt decode (seq_group == nullptr otherwise).
+  const int32_t* seq_group;     // [num_seqs] group of each sequence or -1
+  const int32_t* group_prefix;  // [num_groups] shared prompt tokens of each group
+  int num_groups;
+  int max_group_size;
 };
 
 struct CacheWriteParams {
@@ -52,8 +57,10 @@ struct CacheWriteParams {
   int dtype;
 };
 
-// Byte size of the split-K workspace for these sizes: partials and plan.
-size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions);
+// Byte size of the split-K workspace for these sizes: partials and plan
+// (num_groups > 0 adds the shared-prompt group tables).
+size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions,
+                              int num_groups);
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
 // Single pass when p.workspace == nullptr (then p.max_partitions must be 1).
