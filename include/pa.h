@@ -62,7 +62,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = 2,   /* a size or relation between sizes is invalid */
   PA_ERR_UNSUPPORTED = 3,   /* head_dim, block_size or dtype not built */
   PA_ERR_WORKSPACE = 4,     /* split-K workspace missing or too small */
-  PA_ERR_HIP = 5            /* the HIP runtime reported an error on launch */
+  PA_ERR_HIP = 5,           /* the HIP runtime reported an error on launch */
+  PA_ERR_OUT_OF_BLOCKS = 6  /* block manager: too few free blocks, nothing changed */
 } pa_status;
 
 /* Decode flag bits.
@@ -222,6 +223,35 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
                             int dtype, int num_groups, int max_group_size, int partition_size,
                             int max_context_len, void* workspace, size_t workspace_bytes,
                             int flags, void* stream);
+
+/*
+ * pa_copy_blocks -- copy whole blocks of both pools, every KV head:
+ * for i < num_pairs, block pairs[i][1] of k_pool and v_pool receives the
+ * bytes of block pairs[i][0].  This is the private copy a shared, partly
+ * filled block gets before a request writes into it (block-level sharing,
+ * "Efficient Memory Management ... paper summary", key feature 2; the
+ * copy-on-write reading of pa_block_manager.h).  `pairs` is a DEVICE array
+ * int32 [num_pairs][2] (at most 65535 pairs).  Pairs naming a block outside
+ * [0, num_blocks) are skipped; destinations must be distinct and must not be
+ * sources of other pairs in the same call.  Asynchronous on `stream`.
+ */
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype,
+                   void* stream);
+
+/*
+ * pa_swap_blocks -- move blocks between a device pool and a host pool (the
+ * CPU blocks of "vLLM's efficiency secret ...", section "Dynamic memory
+ * management", num_cpu_blocks): for i < num_pairs, block pairs[i][1] of
+ * (dst_k, dst_v) receives block pairs[i][0] of (src_k, src_v), each block
+ * `block_bytes` long.  to_host = 1 copies device -> host, 0 host -> device.
+ * `pairs` is a HOST array int32 [num_pairs][2], checked against the pool
+ * sizes (PA_ERR_INVALID_ARG).  Runs of consecutive pairs become one copy.
+ * Host pools should be pinned for the copies to be asynchronous on `stream`.
+ */
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                   const int32_t* pairs, int num_pairs, int num_dst_blocks, int num_src_blocks,
+                   size_t block_bytes, int to_host, void* stream);
 
 /*
  * pa_check_inputs_host -- validate HOST copies of the device data against the

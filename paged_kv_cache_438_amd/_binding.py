@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 import torch
 
 LIB_PATH = pathlib.Path(__file__).resolve().parent / "libpa.so"
-HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "pa.h"
+INCLUDE = pathlib.Path(__file__).resolve().parent.parent / "include"
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_FLAG_SHARED_KV = 1
@@ -35,6 +35,25 @@ _SIGNATURES = {
     "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
                              [ctypes.POINTER(_c_int)]),
     "pa_decode_shared_prefix_workspace_bytes": (_c_size_t, [_c_int] * 6),
+    "pa_copy_blocks": (_c_int, [_c_void_p] * 3 + [_c_int] * 6 + [_c_void_p]),
+    "pa_swap_blocks": (_c_int, [_c_void_p] * 5 + [_c_int] * 3 + [_c_size_t, _c_int, _c_void_p]),
+    # block manager (include/pa_block_manager.h)
+    "pa_bm_create": (_c_int, [_c_int] * 3 + [ctypes.POINTER(_c_void_p)]),
+    "pa_bm_destroy": (None, [_c_void_p]),
+    "pa_bm_can_allocate": (_c_int, [_c_void_p, _c_int]),
+    "pa_bm_allocate": (_c_int, [_c_void_p, _c_int, _c_int]),
+    "pa_bm_append_slot": (_c_int, [_c_void_p, _c_int] + [ctypes.POINTER(ctypes.c_int32)] * 4),
+    "pa_bm_fork": (_c_int, [_c_void_p, _c_int, _c_int]),
+    "pa_bm_free": (_c_int, [_c_void_p, _c_int]),
+    "pa_bm_swap_out": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pa_bm_swap_in": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_int, ctypes.POINTER(_c_int)]),
+    "pa_bm_num_free_blocks": (_c_int, [_c_void_p, _c_int]),
+    "pa_bm_usage_ratio": (ctypes.c_double, [_c_void_p]),
+    "pa_bm_seq_info": (_c_int, [_c_void_p, _c_int] + [ctypes.POINTER(_c_int)] * 3),
+    "pa_bm_refcount": (_c_int, [_c_void_p, _c_int, _c_int]),
+    "pa_bm_fill_batch": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_int, _c_void_p]),
+    "pa_bm_prefix_groups": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_void_p,
+                                     ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "pa_decode_shared_prefix": (_c_int, [_c_void_p] * 8 + [_c_int] * 7 +
                                 [_c_float] + [_c_int] * 5 + [_c_void_p, _c_size_t, _c_int,
                                                               _c_void_p]),
@@ -66,9 +85,12 @@ def load() -> ctypes.CDLL:
 
 
 def header_functions() -> list:
-    """Names of the functions include/pa.h declares."""
-    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+    """Names of the functions the headers in include/ declare."""
+    names = set()
+    for h in sorted(INCLUDE.glob("*.h")):
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def status_str(status: int) -> str:
@@ -253,6 +275,46 @@ def pa_decode_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
         PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
     _check(st, "pa_decode_shared_prefix")
     return out
+
+
+def pa_copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
+                   stream=None) -> None:
+    """Copy whole blocks of both pools: pairs int32 [n][2] (source,
+    destination) on the device.  See pa_copy_blocks in include/pa.h."""
+    for n, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(t, n)
+    _dev(pairs, "pairs", torch.int32)
+    NB, Hkv, bs, d = _pool_shape(k_pool, v_pool)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [num_pairs][2]")
+    st = load().pa_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), pairs.data_ptr(),
+                               pairs.shape[0], Hkv, d, bs, NB, _DTYPES.get(k_pool.dtype, -1),
+                               _stream(k_pool.device, stream))
+    _check(st, "pa_copy_blocks")
+
+
+def pa_swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
+                   src_v: torch.Tensor, pairs, stream=None) -> None:
+    """Move blocks between a device pool and a host pool (one of each);
+    pairs [n][2] (source block, destination block) on the host."""
+    import numpy as np
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("pools must share [num_kv_heads][block_size][head_dim]")
+    if dst_k.dtype != src_k.dtype:
+        raise TypeError("pools must share one dtype")
+    for t in (dst_k, dst_v, src_k, src_v):
+        if not t.is_contiguous():
+            raise ValueError("pools must be contiguous")
+    if dst_k.device.type == src_k.device.type:
+        raise ValueError("one pool must be on the host and one on the device")
+    to_host = 1 if dst_k.device.type == "cpu" else 0
+    dev = src_k.device if to_host else dst_k.device
+    pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    block_bytes = dst_k[0].numel() * dst_k.element_size()
+    st = load().pa_swap_blocks(dst_k.data_ptr(), dst_v.data_ptr(), src_k.data_ptr(),
+                               src_v.data_ptr(), pr.ctypes.data, pr.shape[0], dst_k.shape[0],
+                               src_k.shape[0], block_bytes, to_host, _stream(dev, stream))
+    _check(st, "pa_swap_blocks")
 
 
 def pa_check_inputs_host(block_tables, context_lens, block_size: int, num_blocks: int,

@@ -10,13 +10,14 @@
 #include <string>
 #include <unordered_set>
 
+#include "pa_errors.h"
 #include "pa_launch.h"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
-int fail(int status, const char* fmt, ...) {
+int pa_fail(int status, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -26,10 +27,12 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
-int ok() {
+int pa_ok() {
   g_last_error.clear();
   return PA_OK;
 }
+
+namespace {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -37,19 +40,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_common(int num_seqs, int num_kv_heads, int head_dim, int block_size,
                  int max_blocks_per_seq, int num_blocks, int dtype) {
-  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
-  if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", num_kv_heads);
+  if (num_seqs < 0) return pa_fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_kv_heads <= 0) return pa_fail(PA_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", num_kv_heads);
   if (max_blocks_per_seq <= 0)
-    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
-  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", num_blocks);
+    return pa_fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0 (got %d)", max_blocks_per_seq);
+  if (num_blocks <= 0) return pa_fail(PA_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", num_blocks);
   if (head_dim != 64 && head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+    return pa_fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
   if (!is_pow2(block_size) || block_size > 1024)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (power of two in [1,1024])", block_size);
+    return pa_fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (power of two in [1,1024])", block_size);
   if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    return pa_fail(PA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if ((long long)max_blocks_per_seq * block_size > 0x3fffffffLL)
-    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
+    return pa_fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * block_size too large");
   return PA_OK;
 }
 
@@ -60,20 +63,20 @@ int check_decode(const void* out, const void* q, const void* k_pool, const void*
   int st = check_common(num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, dtype);
   if (st) return st;
-  if (num_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_heads must be > 0 (got %d)", num_heads);
+  if (num_heads <= 0) return pa_fail(PA_ERR_INVALID_ARG, "num_heads must be > 0 (got %d)", num_heads);
   if (num_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+    return pa_fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
                 num_kv_heads);
-  if (flags & ~(PA_FLAG_SHARED_KV | PA_FLAG_VALU_ONLY)) return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (flags & ~(PA_FLAG_SHARED_KV | PA_FLAG_VALU_ONLY)) return pa_fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
   if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    return pa_fail(PA_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
-    return fail(PA_ERR_NULL, "a required pointer is NULL");
+    return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return fail(PA_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
+    return pa_fail(PA_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
   if (!aligned16(out))
-    return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    return pa_fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned");
   return PA_OK;
 }
 
@@ -110,8 +113,8 @@ pa::DecodeParams make_params(void* out, const void* q, const void* k_pool, const
 }
 
 int finish_launch(hipError_t e) {
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+  if (e != hipSuccess) return pa_fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return pa_ok();
 }
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -130,6 +133,7 @@ const char* pa_status_str(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_OUT_OF_BLOCKS: return "too few free blocks";
     default: return "unknown status";
   }
 }
@@ -143,11 +147,11 @@ int pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_
   int st = check_common(num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                         num_blocks, dtype);
   if (st) return st;
-  if (num_seqs == 0) return ok();
+  if (num_seqs == 0) return pa_ok();
   if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens)
-    return fail(PA_ERR_NULL, "a required pointer is NULL");
+    return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
-    return fail(PA_ERR_INVALID_ARG, "pools and new rows must be 16-byte aligned");
+    return pa_fail(PA_ERR_INVALID_ARG, "pools and new rows must be 16-byte aligned");
   pa::CacheWriteParams p;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
@@ -174,7 +178,7 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                         dtype, flags);
   if (st) return st;
-  if (num_seqs == 0) return ok();
+  if (num_seqs == 0) return pa_ok();
   pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                                    num_heads, num_kv_heads, head_dim, block_size,
                                    max_blocks_per_seq, num_blocks, scale, dtype, flags);
@@ -225,30 +229,30 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
                         dtype, flags);
   if (st) return st;
   if (dtype != PA_F16 && dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "shared-prefix decode runs on the matrix cores: fp16 or bf16");
+    return pa_fail(PA_ERR_UNSUPPORTED, "shared-prefix decode runs on the matrix cores: fp16 or bf16");
   if (flags & PA_FLAG_VALU_ONLY)
-    return fail(PA_ERR_INVALID_ARG, "PA_FLAG_VALU_ONLY does not apply to shared-prefix decode");
+    return pa_fail(PA_ERR_INVALID_ARG, "PA_FLAG_VALU_ONLY does not apply to shared-prefix decode");
   if (partition_size <= 0 || partition_size % 16 != 0)
-    return fail(PA_ERR_INVALID_ARG, "partition_size must be a positive multiple of 16 (got %d)",
+    return pa_fail(PA_ERR_INVALID_ARG, "partition_size must be a positive multiple of 16 (got %d)",
                 partition_size);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PA_ERR_INVALID_ARG,
+    return pa_fail(PA_ERR_INVALID_ARG,
                 "max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
                 max_context_len, (long long)max_blocks_per_seq * block_size);
-  if (num_groups < 0) return fail(PA_ERR_INVALID_ARG, "num_groups must be >= 0 (got %d)", num_groups);
+  if (num_groups < 0) return pa_fail(PA_ERR_INVALID_ARG, "num_groups must be >= 0 (got %d)", num_groups);
   if (max_group_size < 1 || max_group_size > num_seqs + (num_seqs == 0))
-    return fail(PA_ERR_INVALID_ARG, "max_group_size %d outside [1, num_seqs]", max_group_size);
+    return pa_fail(PA_ERR_INVALID_ARG, "max_group_size %d outside [1, num_seqs]", max_group_size);
   if ((int64_t)max_group_size * (num_heads / num_kv_heads) > 4096)
-    return fail(PA_ERR_INVALID_ARG, "max_group_size * query heads per KV head exceeds 4096");
-  if (num_seqs == 0) return ok();
+    return pa_fail(PA_ERR_INVALID_ARG, "max_group_size * query heads per KV head exceeds 4096");
+  if (num_seqs == 0) return pa_ok();
   if (!seq_group || (num_groups > 0 && !group_prefix_len))
-    return fail(PA_ERR_NULL, "seq_group and group_prefix_len are required");
+    return pa_fail(PA_ERR_NULL, "seq_group and group_prefix_len are required");
   const size_t need = pa_decode_shared_prefix_workspace_bytes(
       num_seqs, num_heads, head_dim, max_context_len, partition_size, num_groups);
   if (!workspace || workspace_bytes < need)
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+    return pa_fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
                 workspace_bytes, workspace ? "" : ", NULL");
-  if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (!aligned16(workspace)) return pa_fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                                    num_heads, num_kv_heads, head_dim, block_size,
                                    max_blocks_per_seq, num_blocks, scale, dtype, flags);
@@ -273,19 +277,19 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
                         dtype, flags);
   if (st) return st;
   if (partition_size <= 0 || partition_size % 16 != 0)
-    return fail(PA_ERR_INVALID_ARG, "partition_size must be a positive multiple of 16 (got %d)",
+    return pa_fail(PA_ERR_INVALID_ARG, "partition_size must be a positive multiple of 16 (got %d)",
                 partition_size);
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PA_ERR_INVALID_ARG,
+    return pa_fail(PA_ERR_INVALID_ARG,
                 "max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
                 max_context_len, (long long)max_blocks_per_seq * block_size);
-  if (num_seqs == 0) return ok();
+  if (num_seqs == 0) return pa_ok();
   const size_t need = pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim,
                                                        max_context_len, partition_size);
   if (!workspace || workspace_bytes < need)
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+    return pa_fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
                 workspace_bytes, workspace ? "" : ", NULL");
-  if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (!aligned16(workspace)) return pa_fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                                    num_heads, num_kv_heads, head_dim, block_size,
                                    max_blocks_per_seq, num_blocks, scale, dtype, flags);
@@ -296,21 +300,72 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
   return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
+                   int num_kv_heads, int head_dim, int block_size, int num_blocks, int dtype,
+                   void* stream) {
+  int st = check_common(1, num_kv_heads, head_dim, block_size, 1, num_blocks, dtype);
+  if (st) return st;
+  if (num_pairs < 0) return pa_fail(PA_ERR_INVALID_ARG, "num_pairs must be >= 0 (got %d)", num_pairs);
+  if (num_pairs > 65535) return pa_fail(PA_ERR_INVALID_ARG, "at most 65535 pairs per call");
+  if (num_pairs == 0) return pa_ok();
+  if (!k_pool || !v_pool || !pairs) return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool))
+    return pa_fail(PA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  const size_t block_bytes = (size_t)num_kv_heads * block_size * head_dim * (dtype == PA_F32 ? 4 : 2);
+  return finish_launch(pa::launch_copy_blocks(k_pool, v_pool, pairs, num_pairs, num_blocks,
+                                              block_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                   const int32_t* pairs, int num_pairs, int num_dst_blocks, int num_src_blocks,
+                   size_t block_bytes, int to_host, void* stream) {
+  if (num_pairs < 0 || num_dst_blocks < 0 || num_src_blocks < 0 || block_bytes == 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "invalid sizes");
+  if (num_pairs == 0) return pa_ok();
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs)
+    return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
+  for (int i = 0; i < num_pairs; ++i)
+    if (pairs[2 * i] < 0 || pairs[2 * i] >= num_src_blocks || pairs[2 * i + 1] < 0 ||
+        pairs[2 * i + 1] >= num_dst_blocks)
+      return pa_fail(PA_ERR_INVALID_ARG, "pair %d (%d, %d) outside the pools", i, pairs[2 * i],
+                     pairs[2 * i + 1]);
+  const hipMemcpyKind kind = to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // Runs of pairs whose sources and destinations are both consecutive go out
+  // as one copy per pool.
+  for (int i = 0; i < num_pairs;) {
+    int j = i + 1;
+    while (j < num_pairs && pairs[2 * j] == pairs[2 * (j - 1)] + 1 &&
+           pairs[2 * j + 1] == pairs[2 * (j - 1) + 1] + 1)
+      ++j;
+    const size_t bytes = (size_t)(j - i) * block_bytes;
+    const size_t so = (size_t)pairs[2 * i] * block_bytes, dso = (size_t)pairs[2 * i + 1] * block_bytes;
+    hipError_t e = hipMemcpyAsync(static_cast<uint8_t*>(dst_k) + dso,
+                                  static_cast<const uint8_t*>(src_k) + so, bytes, kind, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(static_cast<uint8_t*>(dst_v) + dso, static_cast<const uint8_t*>(src_v) + so,
+                         bytes, kind, st);
+    if (e != hipSuccess) return pa_fail(PA_ERR_HIP, "copy failed: %s", hipGetErrorString(e));
+    i = j;
+  }
+  return pa_ok();
+}
+
 int pa_check_inputs_host(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                          int block_size, int max_blocks_per_seq, int num_blocks,
                          int check_write_targets, int* bad_seq) {
   if (bad_seq) *bad_seq = -1;
   if (num_seqs < 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
-    return fail(PA_ERR_INVALID_ARG, "invalid sizes");
-  if (num_seqs == 0) return ok();
-  if (!block_tables || !context_lens) return fail(PA_ERR_NULL, "a required pointer is NULL");
+    return pa_fail(PA_ERR_INVALID_ARG, "invalid sizes");
+  if (num_seqs == 0) return pa_ok();
+  if (!block_tables || !context_lens) return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
   const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
   std::unordered_set<int64_t> slots;
   for (int s = 0; s < num_seqs; ++s) {
     const int64_t L = context_lens[s];
     if (L < 0 || L > cap) {
       if (bad_seq) *bad_seq = s;
-      return fail(PA_ERR_INVALID_ARG, "sequence %d: length %lld outside [0, %lld]", s,
+      return pa_fail(PA_ERR_INVALID_ARG, "sequence %d: length %lld outside [0, %lld]", s,
                   (long long)L, (long long)cap);
     }
     const int64_t nb = ceil_div64(L, block_size);
@@ -318,7 +373,7 @@ int pa_check_inputs_host(const int32_t* block_tables, const int32_t* context_len
     for (int64_t i = 0; i < nb; ++i) {
       if (row[i] < 0 || row[i] >= num_blocks) {
         if (bad_seq) *bad_seq = s;
-        return fail(PA_ERR_INVALID_ARG, "sequence %d: block table entry %lld = %d outside [0, %d)",
+        return pa_fail(PA_ERR_INVALID_ARG, "sequence %d: block table entry %lld = %d outside [0, %d)",
                     s, (long long)i, row[i], num_blocks);
       }
     }
@@ -327,13 +382,13 @@ int pa_check_inputs_host(const int32_t* block_tables, const int32_t* context_len
       const int64_t slot = (int64_t)row[pos / block_size] * block_size + pos % block_size;
       if (!slots.insert(slot).second) {
         if (bad_seq) *bad_seq = s;
-        return fail(PA_ERR_INVALID_ARG,
+        return pa_fail(PA_ERR_INVALID_ARG,
                     "sequence %d: new-token slot (block %d, row %lld) already written by another "
                     "sequence", s, row[pos / block_size], (long long)(pos % block_size));
       }
     }
   }
-  return ok();
+  return pa_ok();
 }
 
 }  // extern "C"

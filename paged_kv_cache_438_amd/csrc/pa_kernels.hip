@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_launch.h"
@@ -443,6 +444,16 @@ struct BlockIds {
   int nxt[BIG_BLOCKS ? 1 : NR];
 };
 
+// Register buffers of the vector-ALU kernel's pipeline (2 or 3).
+#ifndef PA_VALU_STAGES
+#define PA_VALU_STAGES 2
+#endif
+// Waves per workgroup of the vector-ALU kernel's single pass with one head
+// per wave.
+#ifndef PA_VALU_SINGLE_WAVES
+#define PA_VALU_SINGLE_WAVES 16
+#endif
+
 // One workgroup = (sequence s, KV head g, chunk of GW query heads, partition p).
 // Its W waves take the partition's 16-token steps round-robin.
 template <int DT, int D, int W, int GW, bool BIG_BLOCKS, bool NT>
@@ -577,7 +588,11 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   };
 
   if (nk > 0) fetch_ids(0);
+#if PA_VALU_STAGES == 3
+  run_pipeline3<Buf>(nk, load_step, compute_step);
+#else
   run_pipeline<Buf>(nk, load_step, compute_step);
+#endif
 
   // Merge the row groups of this wave.
 #pragma unroll
@@ -1259,6 +1274,35 @@ __global__ __launch_bounds__(256) void k_cache_write(const CArgs a) {
   *reinterpret_cast<uint4*>(a.v_pool + dst) = *reinterpret_cast<const uint4*>(a.v_new + src);
 }
 
+struct BArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const int32_t* pairs;   // [n][2] (source block, destination block)
+  int num_pairs, num_blocks;
+  size_t block_bytes;     // num_kv_heads * block_size * head_dim * elem, a multiple of 16
+};
+
+// Copy whole blocks of both pools (every KV head), e.g. the private copy a
+// shared, partly filled block gets before a write.  Workgroup (pair, piece):
+// 256 threads move 16-byte chunks of one block with streaming loads and
+// stores.  Pairs naming a block outside the pool are skipped.
+__global__ __launch_bounds__(256) void k_copy_blocks(const BArgs a) {
+  const int pair = blockIdx.y;
+  const int src = a.pairs[2 * pair], dst = a.pairs[2 * pair + 1];
+  if ((unsigned)src >= (unsigned)a.num_blocks || (unsigned)dst >= (unsigned)a.num_blocks ||
+      src == dst)
+    return;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const size_t n16 = a.block_bytes / 16;
+  const size_t so = (size_t)src * a.block_bytes, dso = (size_t)dst * a.block_bytes;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+    const u32x4 k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_pool + so) + i);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v_pool + so) + i);
+    __builtin_nontemporal_store(k, reinterpret_cast<u32x4*>(a.k_pool + dso) + i);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.v_pool + dso) + i);
+  }
+}
+
 int ilog2(int x) {
   int r = 0;
   while ((1 << r) < x) ++r;
@@ -1424,7 +1468,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   // partition of P tokens has P/16 steps; keep at least four per wave.
   int waves;
   const int row_bytes = p.head_dim * (p.dtype == kF32 ? 4 : 2);
-  if (p.workspace == nullptr) waves = gw == 1 && row_bytes <= 256 ? 16 : 8;
+  if (p.workspace == nullptr) waves = gw == 1 && row_bytes <= 256 ? PA_VALU_SINGLE_WAVES : 8;
   else waves = p.partition_size >= 512 ? 8 : 4;
   const long long units = p.workspace == nullptr
                               ? p.num_seqs
@@ -1465,6 +1509,22 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     case kF16: return launch_reduce_t<kF16>(ka, p.head_dim, rgrid, stream);
     default: return launch_reduce_t<kBF16>(ka, p.head_dim, rgrid, stream);
   }
+}
+
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
+                              int num_blocks, size_t block_bytes, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  BArgs a;
+  a.k_pool = static_cast<uint8_t*>(k_pool);
+  a.v_pool = static_cast<uint8_t*>(v_pool);
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  a.block_bytes = block_bytes;
+  const size_t chunks = block_bytes / 16;
+  const int pieces = (int)std::min<size_t>((chunks + 1023) / 1024, 64);   // 4 chunks per thread
+  hipLaunchKernelGGL(k_copy_blocks, dim3(pieces, num_pairs), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
