@@ -115,6 +115,11 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="override the workload's block size (page-size sweep)")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="one block per sequence, as long as the longest possible sequence: "
+                         "the contiguous per-sequence cache the pages contrast paging with")
     ap.add_argument("--cached", action="store_true",
                     help="plain cached K/V loads (the shared-blocks policy) even without sharing")
     ap.add_argument("--valu-only", action="store_true",
@@ -144,6 +149,16 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     entry, P = DEFAULT_ENTRY[w.name]
+    if args.contiguous or args.block_size:
+        longest = w.length_hi if w.length_kind != "shared_prefix" else w.prompt_len + w.length_hi
+        if w.length_kind == "fixed":
+            longest = max(w.lengths)
+        bs = args.block_size or 1 << (longest - 1).bit_length()
+        if args.contiguous and bs < longest:
+            raise SystemExit("--contiguous needs a block at least as long as the longest sequence")
+        if w.length_kind == "shared_prefix" and w.prompt_len % bs:
+            raise SystemExit("the shared prompt must be whole blocks")
+        w = w.replace(block_size=bs, max_blocks_per_seq=-(-longest // bs))
     if args.entry:
         entry = args.entry
         P = args.partition or (w.partition_size or 1024) if entry != "single" else None
@@ -272,6 +287,7 @@ def main() -> int:
         "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[dt],
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "seed": case.seed,
+                   "block_size": w.block_size,
                    "entry": ENTRY_NAME[entry],
                    "partition_size": P, "accumulate": "f32", "shared_kv_flag": shared,
                    "valu_only": bool(args.valu_only),

@@ -82,7 +82,9 @@ typedef enum {
 #define PA_FLAG_VALU_ONLY 2
 
 /* Supported shapes: head_dim in {64, 128}; block_size a power of two in
- * [1, 1024]; num_heads a multiple of num_kv_heads; dtype one of pa_dtype. */
+ * [1, 65536] (a block at least as long as a sequence's largest length gives
+ * the contiguous per-sequence cache as a special case); num_heads a multiple
+ * of num_kv_heads; dtype one of pa_dtype. */
 
 /* Version of this ABI (PA_ABI_VERSION of the built library). */
 int pa_abi_version(void);

@@ -47,8 +47,9 @@ int check_common(int num_seqs, int num_kv_heads, int head_dim, int block_size,
   if (num_blocks <= 0) return pa_fail(PA_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", num_blocks);
   if (head_dim != 64 && head_dim != 128)
     return pa_fail(PA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
-  if (!is_pow2(block_size) || block_size > 1024)
-    return pa_fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (power of two in [1,1024])", block_size);
+  if (!is_pow2(block_size) || block_size > 65536)
+    return pa_fail(PA_ERR_UNSUPPORTED, "block_size %d not supported (power of two in [1,65536])",
+                   block_size);
   if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
     return pa_fail(PA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if ((long long)max_blocks_per_seq * block_size > 0x3fffffffLL)

@@ -51,7 +51,7 @@ def _decode(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d=96), 3), (dict(d=256), 3), (dict(bs=12), 3), (dict(bs=2048), 3), (dict(bs=0), 3),
+    (dict(d=96), 3), (dict(d=256), 3), (dict(bs=12), 3), (dict(bs=131072), 3), (dict(bs=0), 3),
     (dict(dtype=7), 3), (dict(Hq=6, Hkv=4), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
     (dict(B=-1), 2), (dict(MB=0), 2), (dict(NB=0), 2), (dict(scale=float("nan")), 2),
     (dict(scale=float("inf")), 2), (dict(q=0), 1), (dict(out=0), 1), (dict(tb=0), 1),

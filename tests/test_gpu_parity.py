@@ -89,6 +89,8 @@ EDGE = [
     ("bs512_bf16", (1, 511, 512, 513, 1023, 1024, 1025, 1600), 2, 2, 128, 512, "bf16", 512),
     ("bs1024_f16_p512", (1, 511, 512, 513, 1024, 1025, 2047, 2048), 2, 1, 64, 1024, "f16", 512),
     ("bs64_f32_d64", (0, 63, 64, 65, 128, 129, 300), 2, 1, 64, 64, "f32", 128),
+    ("bs2048_f16", (1, 2047, 2048, 2049, 3000), 2, 2, 128, 2048, "f16", 1024),
+    ("bs4096_bf16_g4_contiguous", (1, 100, 1500, 4095, 4096), 8, 2, 128, 4096, "bf16", 512),
 ]
 
 
