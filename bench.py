@@ -33,7 +33,7 @@ METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and KV tokens/se
 # partitions, the best trade between balance and per-partition overhead for
 # its log-normal length mix (lengths up to 16384).
 DEFAULT_ENTRY = {"llama2_7b": ("single", None), "long_bs512": ("splitk", 512),
-                 "gqa_70b": ("splitk", 4096), "shared_prefix": ("shared", 1024),
+                 "gqa_70b": ("splitk", 4096), "shared_prefix": ("shared", 2048),
                  "tiny": ("single", None)}
 ENTRY_NAME = {"single": "pa_decode", "splitk": "pa_decode_splitk",
               "shared": "pa_decode_shared_prefix"}
@@ -210,7 +210,10 @@ def main() -> int:
                                                           maxlen, P, len(case.shared_groups))
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-    shared = case.shared_groups is not None or args.cached   # keep K/V loads cached
+    # Cached K/V loads when several sequences' tables name the same blocks and
+    # the kernel reads them once per sequence; the sharing-aware entry reads
+    # a group's prompt once per KV head, so it streams.
+    shared = args.cached or (case.shared_groups is not None and entry != "shared")
 
     def decode():
         if entry == "single":

@@ -205,15 +205,30 @@ size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int 
  * nothing; group_prefix_len[i] is the number of prompt tokens group i shares:
  * a multiple of block_size, at most every member's length, and the first
  * group_prefix_len[i] / block_size entries of every member's table name the
- * same blocks.  Each group has at most max_group_size members.  The member's
- * own tokens [group_prefix_len, L) and ungrouped sequences are processed per
- * sequence.  Every sequence is cut into the prompt's partitions and its own
- * partitions of partition_size tokens, and the partials are merged in fixed
- * order as in pa_decode_splitk, so results do not depend on scheduling.
+ * same blocks.  Each group has at most max_group_size members.
+ *
+ * Work units: the prompt is cut into partitions of partition_size tokens,
+ * each computed once for all members.  A member's own tokens
+ * [group_prefix_len, L) are absorbed into the group's last prompt partition
+ * when there are at most partition_size / m of them, m being the most
+ * members whose query columns share one chunk of 16 (16 / G for G query
+ * heads per KV head dividing 16); that partition then streams each absorbed
+ * member's tokens too, seen only by that member's columns, so it never
+ * holds more than 2 * partition_size tokens.  Other members' own tokens,
+ * and ungrouped sequences, are cut into partitions of their own.  A member
+ * whose only partition is the absorbing one gets its output written
+ * directly; otherwise partials are merged in fixed order as in
+ * pa_decode_splitk.  Results are deterministic: the plan sorts each group's
+ * members by sequence index.  A member's bits may depend on the lengths of
+ * the members sorted before it in its chunk (which wave takes which of its
+ * absorbed steps), not on their K/V values as long as those are finite.
  * A group that breaks the contract gives its members NaN rows.
  *
- * fp16 and bf16 only (PA_ERR_UNSUPPORTED otherwise); PA_FLAG_SHARED_KV is
- * accepted (blocks shared with other calls), PA_FLAG_VALU_ONLY is rejected.
+ * fp16 and bf16 only (PA_ERR_UNSUPPORTED otherwise); PA_FLAG_VALU_ONLY is
+ * rejected.  PA_FLAG_SHARED_KV (cached loads) pays only when one prompt
+ * partition is read by several column chunks, i.e. when a group has more
+ * than 16 query columns (members * G); otherwise each prompt block is read
+ * once per KV head and streaming loads (no flag) are faster.
  * max_context_len, partition_size and the workspace are as for
  * pa_decode_splitk, with pa_decode_shared_prefix_workspace_bytes(...) bytes.
  */

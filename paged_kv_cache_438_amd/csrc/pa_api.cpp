@@ -196,7 +196,7 @@ size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_di
     return 0;
   const int parts = (int)ceil_div64(max_context_len, partition_size);
   const size_t bytes =
-      pa::splitk_workspace_bytes(num_seqs, num_heads, head_dim, parts > 0 ? parts : 1, 0);
+      pa::splitk_workspace_bytes(num_seqs, num_heads, head_dim, parts > 0 ? parts : 1, -1);
   return (bytes + 255) / 256 * 256;
 }
 

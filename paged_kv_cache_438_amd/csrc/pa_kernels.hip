@@ -205,7 +205,8 @@ struct KArgs {
   const int32_t* lens;
   float* ws_acc;        // [B][Hq][max_parts][D]
   float2* ws_ml;        // [B][Hq][max_parts] of (max, sum)
-  const int* n_units;   // split-K plan: number of (sequence, partition) units
+  const int* n_units;   // split-K plan: number of (sequence, partition) units,
+                        // then the number of sequences with several partitions
   const int2* units;    // split-K plan: units, longest first
   // Shared-prompt decode (nullptr otherwise): the group of each sequence
   // (-1: none), each group's shared prompt length, and the members of each
@@ -227,30 +228,59 @@ struct KArgs {
 // are cut into partitions of P tokens.  A sequence whose group shares a
 // prompt of Lp tokens (a multiple of the block size, the same blocks at the
 // head of every member's table) has the prompt's partitions first -- they
-// are computed once for the whole group -- then its own tokens [Lp, L) in
-// partitions of P.  Out-of-contract sequences get no partitions and a NaN
-// output row.
+// are computed once for the whole group.  Its own tokens [Lp, L) follow in
+// partitions of P, unless they are few enough to be absorbed into the
+// group's last prompt partition: at most P / m tokens, where m bounds the
+// members one column chunk holds, so that partition never streams more
+// than P prompt tokens plus P own tokens.  Out-of-contract sequences get no
+// partitions and a NaN output row.
 struct SeqLayout {
   int len, lp, np_pre, nparts;
-  bool bad;
+  bool bad, absorbed;
 };
-__device__ __forceinline__ SeqLayout seq_layout(const KArgs& a, int s) {
+// Most members whose query columns share one chunk of 16 (a member has
+// `group` consecutive columns).
+__device__ __forceinline__ int members_per_chunk(int group) {
+  return 16 % group == 0 ? 16 / group : 16 / group + 2;
+}
+// Layout from a sequence's length and group (-1: none); for a group in
+// range, lp_g is its prompt length and cnt its member count.
+__device__ __forceinline__ SeqLayout layout_of(const KArgs& a, int len, int gi, int lp_g, int cnt) {
   SeqLayout r;
-  r.len = a.lens[s];
+  r.len = len;
   r.lp = 0;
+  r.absorbed = false;
   bool bad = r.len < 0 || r.len > (a.max_blocks << a.bs_log2);
   if (a.seq_group != nullptr) {
-    const int gi = a.seq_group[s];
     if (gi >= a.num_groups || gi < -1) bad = true;
-    else if (gi >= 0) r.lp = a.group_prefix[gi];
+    else if (gi >= 0) r.lp = lp_g;
     if (r.lp < 0 || r.lp > r.len || (r.lp & ((1 << a.bs_log2) - 1)) != 0) bad = true;
   }
   if (bad) { r.len = 0; r.lp = 0; }
   r.np_pre = (r.lp + a.part_tokens - 1) / a.part_tokens;
-  r.nparts = r.np_pre + (r.len - r.lp + a.part_tokens - 1) / a.part_tokens;
-  if (r.nparts > a.max_parts) { bad = true; r.len = r.lp = r.np_pre = r.nparts = 0; }
+  if (r.lp > 0) {
+    const int m = max(1, min(cnt, members_per_chunk(a.group)));
+    r.absorbed = r.len - r.lp <= a.part_tokens / m;
+  }
+  r.nparts = r.np_pre + (r.absorbed ? 0 : (r.len - r.lp + a.part_tokens - 1) / a.part_tokens);
+  if (r.nparts > a.max_parts) {
+    bad = true;
+    r.len = r.lp = r.np_pre = r.nparts = 0;
+    r.absorbed = false;
+  }
   r.bad = bad;
   return r;
+}
+__device__ __forceinline__ SeqLayout seq_layout(const KArgs& a, int s) {
+  int gi = -1, lp = 0, cnt = 0;
+  if (a.seq_group != nullptr) {
+    gi = a.seq_group[s];
+    if (gi >= 0 && gi < a.num_groups) {
+      lp = a.group_prefix[gi];
+      cnt = a.group_start[gi + 1] - a.group_start[gi];
+    }
+  }
+  return layout_of(a, a.lens[s], gi, lp, cnt);
 }
 
 // One query column of a matrix-core workgroup: whose query it is, which
@@ -265,10 +295,12 @@ struct Col {
 // columns, the sequence whose table supplies the blocks, and the token range.
 // A prompt unit (prompt_group >= 0) covers one partition of a group's shared
 // prompt for all members at once: column c is member c / G, query head
-// g*G + c % G.  Otherwise the columns are query heads of one sequence.
+// g*G + c % G.  The last prompt partition (tail) also streams the absorbed
+// own tokens of the chunk's members.  Otherwise the columns are query heads
+// of one sequence.
 struct KUnit {
   int ch, g, ts, t_begin, t_end, prompt_group, s, p, ncols;
-  bool bad;
+  bool bad, tail;
 };
 __device__ __forceinline__ bool resolve_kunit(const KArgs& a, KUnit& u, SeqLayout& lay) {
   int wg = blockIdx.x;
@@ -292,6 +324,7 @@ __device__ __forceinline__ bool resolve_kunit(const KArgs& a, KUnit& u, SeqLayou
     u.p = y;
     u.t_begin = y * a.part_tokens;
     u.t_end = min(u.t_begin + a.part_tokens, lp);
+    u.tail = u.t_end == lp;
     u.ncols = min(16, cnt * a.group - u.ch * 16);
   } else {
     lay = seq_layout(a, x);
@@ -299,6 +332,7 @@ __device__ __forceinline__ bool resolve_kunit(const KArgs& a, KUnit& u, SeqLayou
     u.ts = u.s = x;
     u.p = y;
     u.bad = lay.bad;
+    u.tail = false;
     u.t_begin = lay.lp + (y - lay.np_pre) * a.part_tokens;
     u.t_end = min(u.t_begin + a.part_tokens, lay.len);
     if (lay.nparts == 0) u.t_begin = u.t_end = 0;
@@ -830,11 +864,71 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
   SeqLayout lay;
   if (!resolve_kunit(a, un, lay)) return;
   const int g = un.g;
-  const int t_begin = un.t_begin, t_end = un.t_end;
-  const int nsteps = t_end > t_begin ? (t_end - t_begin + 15) >> 4 : 0;
   const int nh = un.ncols;                       // columns in use in this chunk
   const Col col = column_of(a, un, lay, n);      // this lane's column
   uint4 qv[NI];                                  // Q^T operand, loaded below
+
+  // Token streams of the workgroup, 16-token steps each.  Stream 0 is the
+  // unit's token range through the table of sequence un.ts.  A group's last
+  // prompt partition adds one stream per member of the chunk, holding that
+  // member's absorbed own tokens through its own table; only that member's
+  // columns see them (the others get weight exactly 0).  Lane i describes
+  // stream i: first step, token range, sequence, member index (-1: every
+  // column).  Global step j goes to wave j % W.
+  const int cc0 = un.ch * 16;
+  const int col_mi = (cc0 + n) / a.group;        // member index of this lane's column
+  int st_first, st_tb = 0, st_te = 0, st_seq = un.ts, st_mi = -1;
+  {
+    if (lane == 0) {
+      st_tb = un.t_begin;
+      st_te = un.t_end;
+    } else if (un.tail) {
+      const int mi_lo = cc0 / a.group;
+      const int nm = (cc0 + nh - 1) / a.group - mi_lo + 1;
+      if (lane <= nm) {
+        const int first = a.group_start[un.prompt_group];
+        st_mi = mi_lo + lane - 1;
+        st_seq = a.members[first + st_mi];
+        const SeqLayout ml = seq_layout(a, st_seq);
+        if (!ml.bad && ml.absorbed) {
+          st_tb = ml.lp;
+          st_te = ml.len;
+        }
+      }
+    }
+    const int cnt = st_te > st_tb ? (st_te - st_tb + 15) >> 4 : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    st_first = incl - cnt;
+  }
+  const int nsteps = __builtin_amdgcn_readlane(st_first + (st_te > st_tb ? (st_te - st_tb + 15) >> 4 : 0), 63);
+  struct StepAt { int t0, t_end, mi; const_i32_ptr trow; };
+  // The stream of a step is the highest lane whose first step is not after
+  // it (streams without steps share the next stream's first step).
+  auto step_at = [&](int k) {
+    const int j = wave + k * W;
+    StepAt r;
+    if (!un.tail) {
+      r.t0 = un.t_begin + (j << 4);
+      r.t_end = un.t_end;
+      r.mi = -1;
+      r.trow = (const_i32_ptr)(a.tables + (size_t)un.ts * a.max_blocks);
+    } else {
+      const uint64_t le = __builtin_amdgcn_ballot_w64(st_first <= j);
+      const int si = 63 - __builtin_clzll(le);
+      r.t0 = __builtin_amdgcn_readlane(st_tb, si) +
+             ((j - __builtin_amdgcn_readlane(st_first, si)) << 4);
+      r.t_end = __builtin_amdgcn_readlane(st_te, si);
+      r.mi = __builtin_amdgcn_readlane(st_mi, si);
+      r.trow = (const_i32_ptr)(a.tables +
+                               (size_t)__builtin_amdgcn_readlane(st_seq, si) * a.max_blocks);
+    }
+    return r;
+  };
 
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
   uint8_t* wave_lds = s_dyn + wave * 2 * SLOT;
@@ -849,28 +943,27 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
   const int bs_mask = (1 << a.bs_log2) - 1;
   const size_t tile_bytes = (size_t)ROWB << a.bs_log2;
   const size_t block_bytes = tile_bytes * a.num_kv_heads;
-  const const_i32_ptr trow = (const_i32_ptr)(a.tables + (size_t)un.ts * a.max_blocks);
   bool bad_block = false;
 
   const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
-  auto step_t0 = [&](int k) { return t_begin + ((wave + k * W) << 4); };
   // Row of the step this lane loads with instruction j (clamped to the last
   // valid row past the end), and its position in the slot row.
   const int lrow = lane / LPR;
   const int lpos = lane % LPR;
   BlockIds<BIG_BLOCKS, NDMA> ids;
   auto fetch_ids = [&](int k) {
-    const int t0 = step_t0(k);
+    const StepAt st = step_at(k);
     if constexpr (BIG_BLOCKS) {
-      ids.nxt[0] = trow[t0 >> a.bs_log2];
+      ids.nxt[0] = st.trow[st.t0 >> a.bs_log2];
     } else {
 #pragma unroll
       for (int j = 0; j < NDMA; ++j)
-        ids.nxt[j] = trow[min(t0 + j * RPI + lrow, t_end - 1) >> a.bs_log2];
+        ids.nxt[j] = st.trow[min(st.t0 + j * RPI + lrow, st.t_end - 1) >> a.bs_log2];
     }
   };
   auto issue = [&](int k, int slot) {
-    const int t0 = step_t0(k);
+    const StepAt st = step_at(k);
+    const int t0 = st.t0, t_end = st.t_end;
 #pragma unroll
     for (int i = 0; i < (BIG_BLOCKS ? 1 : NDMA); ++i) ids.cur[i] = ids.nxt[i];
     fetch_ids(k + 1 < nk ? k + 1 : k);
@@ -903,13 +996,15 @@ __global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
     return o;
   };
   auto compute_step = [&](int k, const Ops& b) {
-    const int t0 = step_t0(k);
+    const StepAt st = step_at(k);
+    const bool mine = st.mi < 0 || st.mi == col_mi;
     f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NI; ++i) sc = Mma<DT>::qk(b.k[i], qv[i], sc);
     float z[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = (t0 + 4 * lg + r < t_end) ? sc[r] * a.scale_log2 : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+      z[r] = (mine && st.t0 + 4 * lg + r < st.t_end) ? sc[r] * a.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -1085,66 +1180,121 @@ __device__ __forceinline__ void block_exclusive_scan(const int* src, int* dst, i
   if (tid == 0) dst[n] = carry;
 }
 
+// Sequences and groups whose data the plan keeps in LDS (61 KiB in all);
+// beyond these counts it reads and writes global memory instead.
+constexpr int kPlanSeqs = 4096;
+constexpr int kPlanGroups = 1024;
+
 // Split-K plan, one workgroup.  Every sequence contributes its own
 // partitions (at least one unit, so that empty or out-of-contract sequences
 // still write their row); with shared prompts every group also contributes
 // the partitions of its prompt, each a single unit for all members.  The
 // units are counting-sorted by size into 256 buckets, largest first, so the
 // partition kernel's workgroups are dispatched longest first (longest-first
-// list scheduling).  The order inside a bucket and the order of a group's
-// members depend on timing; no result does, because every column's
-// arithmetic and the reduce's order are fixed.
+// list scheduling).  The order inside a bucket depends on timing; no result
+// does, because every column's arithmetic, the streams of a unit (members
+// in ascending sequence order) and the reduce's order are fixed.
+// Lengths, groups and group tables are staged in LDS, so the phases below
+// touch global memory only to load them and to write the plan.
 __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
   __shared__ int hist[257];           // bucket counts, then starts (+ total)
   __shared__ int s_tot[16];
+  __shared__ int s_split;             // sequences with more than one partition
+  __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_arr[kPlanSeqs];
+  __shared__ int s_gfill[kPlanGroups], s_gstart[kPlanGroups + 1], s_glp[kPlanGroups];
   const int tid = threadIdx.x;
-  const int P = pa.k.part_tokens;
-  const bool shared = pa.k.seq_group != nullptr;
-  const int NG = shared ? pa.k.num_groups : 0;
+  const KArgs a = pa.k;
+  const int P = a.part_tokens;
+  const int B = a.num_seqs;
+  const bool shared = a.seq_group != nullptr;
+  const int NG = shared ? a.num_groups : 0;
+  const bool lds_groups = NG <= kPlanGroups;
+  int* gfill = lds_groups ? s_gfill : pa.group_fill;
+  int* gstart = lds_groups ? s_gstart : pa.group_start;
+  int* glp = lds_groups ? s_glp : pa.group_lp;
   if (tid < 256) hist[tid] = 0;
-  for (int i = tid; i < NG; i += 1024) pa.group_fill[i] = 0;
+  if (tid == 0) s_split = 0;
+  for (int i = tid; i < NG; i += 1024) gfill[i] = 0;
+  for (int s = tid; s < min(B, kPlanSeqs); s += 1024) {
+    s_len[s] = a.lens[s];
+    s_grp[s] = shared ? a.seq_group[s] : -1;
+  }
   __syncthreads();
-  KArgs a = pa.k;
+  auto len_of = [&](int s) { return s < kPlanSeqs ? s_len[s] : a.lens[s]; };
+  auto grp_of = [&](int s) { return !shared ? -1 : (s < kPlanSeqs ? s_grp[s] : a.seq_group[s]); };
+  auto layout = [&](int s) {
+    const int gi = grp_of(s);
+    int lp = 0, cnt = 0;
+    if (gi >= 0 && gi < NG) {
+      lp = glp[gi];
+      cnt = gstart[gi + 1] - gstart[gi];
+    }
+    return layout_of(a, len_of(s), gi, lp, cnt);
+  };
   if (shared) {
     // Members of each group, grouped by a counting sort.
-    for (int s = tid; s < a.num_seqs; s += 1024) {
-      const int gi = a.seq_group[s];
-      if (gi >= 0 && gi < NG) atomicAdd(&pa.group_fill[gi], 1);
+    for (int s = tid; s < B; s += 1024) {
+      const int gi = grp_of(s);
+      if (gi >= 0 && gi < NG) atomicAdd(&gfill[gi], 1);
     }
     __syncthreads();
-    block_exclusive_scan(pa.group_fill, pa.group_start, NG, s_tot);
+    block_exclusive_scan(gfill, gstart, NG, s_tot);
     __syncthreads();
     for (int i = tid; i < NG; i += 1024) {
       // A prompt that is not whole blocks, longer than a table can hold, cut
       // into more partitions than a sequence may have, or shared by more
       // members than the launch's column chunks cover is out of contract:
       // it is marked invalid (-1), so its members get NaN rows.
-      const int cnt = pa.group_fill[i];
+      const int cnt = gfill[i];
       const int lp = a.group_prefix[i];
       const bool ok = cnt <= pa.max_group_size && lp >= 0 &&
                       lp <= (a.max_blocks << a.bs_log2) &&
                       (lp & ((1 << a.bs_log2) - 1)) == 0 && (lp + P - 1) / P <= a.max_parts;
-      pa.group_lp[i] = ok ? lp : -1;
-      pa.group_fill[i] = 0;
+      glp[i] = ok ? lp : -1;
+      gfill[i] = 0;
     }
     __syncthreads();
-    for (int s = tid; s < a.num_seqs; s += 1024) {
-      const int gi = a.seq_group[s];
-      if (gi >= 0 && gi < NG) pa.members[pa.group_start[gi] + atomicAdd(&pa.group_fill[gi], 1)] = s;
+    // Members in ascending sequence order, so which member's own tokens a
+    // workgroup streams at which step does not depend on timing: first in
+    // arrival order, then each placed at its rank among its group's members.
+    const int nmem = gstart[NG];
+    int* arrival = nmem <= kPlanSeqs ? s_arr : reinterpret_cast<int*>(pa.units);
+    for (int s = tid; s < B; s += 1024) {
+      const int gi = grp_of(s);
+      if (gi >= 0 && gi < NG) arrival[gstart[gi] + atomicAdd(&gfill[gi], 1)] = s;
     }
     __syncthreads();
-    a.group_prefix = pa.group_lp;
-    a.group_start = pa.group_start;
-    a.members = pa.members;
+    for (int x = tid; x < nmem; x += 1024) {
+      const int s = arrival[x];
+      const int gi = grp_of(s);
+      const int lo = gstart[gi], hi = gstart[gi + 1];
+      int rank = 0;
+      for (int y = lo; y < hi; ++y) rank += arrival[y] < s;
+      pa.members[lo + rank] = s;
+    }
+    for (int i = tid; i < NG; i += 1024) gfill[i] = 0;
+    __syncthreads();
+    // gfill[gi] <- absorbed own tokens of the group per column chunk (at
+    // most about P by the absorption bound).
+    for (int s = tid; s < B; s += 1024) {
+      const SeqLayout ml = layout(s);
+      if (ml.bad || !ml.absorbed) continue;
+      const int gi = grp_of(s);
+      const int cnt = gstart[gi + 1] - gstart[gi];
+      atomicAdd(&gfill[gi], (ml.len - ml.lp) / ((cnt * a.group + 15) / 16));
+    }
+    __syncthreads();
   }
+  // Units hold up to 2P tokens (a last prompt partition with absorbed own
+  // tokens); buckets split [0, 2P] evenly, largest first.
   auto bucket = [&](int size) {
-    const long long b = ((long long)(P - size) * 256) / P;
-    return (int)(b > 255 ? 255 : b);
+    const long long b = ((long long)(2 * P - size) * 256) / (2 * P);
+    return (int)(b < 0 ? 0 : (b > 255 ? 255 : b));
   };
   // Prompt partitions of a group: np_pre units, the last holding the rest.
   auto prompt_parts = [&](int gi) {
-    const int cnt = pa.group_start[gi + 1] - pa.group_start[gi];
-    const int lp = a.group_prefix[gi];
+    const int cnt = gstart[gi + 1] - gstart[gi];
+    const int lp = glp[gi];
     if (cnt == 0 || lp <= 0) return 0;
     return (lp + P - 1) / P;
   };
@@ -1157,11 +1307,14 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
     };
     for (int gi = tid; gi < NG; gi += 1024) {
       const int np = prompt_parts(gi);
-      for (int q = 0; q < np; ++q) put(min(P, a.group_prefix[gi] - q * P), -(gi + 1), q);
+      for (int q = 0; q + 1 < np; ++q) put(P, -(gi + 1), q);
+      // the last partition: the rest of the prompt plus absorbed own tokens
+      if (np > 0) put(glp[gi] - (np - 1) * P + gfill[gi], -(gi + 1), np - 1);
     }
-    for (int s = tid; s < a.num_seqs; s += 1024) {
-      const SeqLayout lay = seq_layout(a, s);
+    for (int s = tid; s < B; s += 1024) {
+      const SeqLayout lay = layout(s);
       const int own = lay.nparts - lay.np_pre;
+      if (pass == 0 && lay.nparts > 1) atomicAdd(&s_split, 1);
       if (lay.nparts == 0) put(0, s, 0);
       for (int q = 0; q < own; ++q)
         put(min(P, lay.len - lay.lp - q * P), s, lay.np_pre + q);
@@ -1171,9 +1324,17 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
       // bucket counts -> bucket starts; hist[256] = number of units
       block_exclusive_scan(hist, hist, 256, s_tot);
       __syncthreads();
-      if (tid == 0) *pa.n_units = hist[256];
+      if (tid == 0) {
+        pa.n_units[0] = hist[256];
+        pa.n_units[1] = s_split;      // 0: the reduce launch has nothing to do
+      }
       __syncthreads();
     }
+  }
+  // The group tables the partition and reduce launches read.
+  if (shared && lds_groups) {
+    for (int i = tid; i <= NG; i += 1024) pa.group_start[i] = gstart[i];
+    for (int i = tid; i < NG; i += 1024) pa.group_lp[i] = glp[i];
   }
 }
 
@@ -1199,7 +1360,7 @@ __global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
   constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.num_seqs * a.num_heads) return;
+  if (item >= a.num_seqs * a.num_heads || a.n_units[1] == 0) return;
   const int s = item / a.num_heads;
   const SeqLayout lay = seq_layout(a, s);
   if (lay.bad || lay.nparts <= 1) return;   // written by the partition kernel
@@ -1396,8 +1557,11 @@ struct WsLayout {
   size_t ml, n_units, units, group_fill, group_start, members, group_lp, total;
 };
 static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+// num_groups < 0: a plain split-K call, no group tables.
 static WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_partitions,
                           int num_groups) {
+  const bool tables = num_groups >= 0;
+  if (num_groups < 0) num_groups = 0;
   WsLayout w;
   const size_t slots = (size_t)num_seqs * num_heads * max_partitions;
   w.ml = slots * head_dim * sizeof(float);
@@ -1408,7 +1572,7 @@ static WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_par
   w.members = up256(w.group_start + (size_t)(num_groups + 1) * sizeof(int));
   w.group_lp = up256(w.members + (size_t)num_seqs * sizeof(int));
   w.total = up256(w.group_lp + (size_t)num_groups * sizeof(int));
-  if (num_groups == 0) w.total = w.group_fill;
+  if (!tables) w.total = w.group_fill;
   return w;
 }
 
@@ -1429,7 +1593,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.lens = p.context_lens;
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
   const WsLayout wl = ws_layout(p.num_seqs, p.num_heads, p.head_dim, p.max_partitions,
-                                shared ? p.num_groups : 0);
+                                shared ? p.num_groups : -1);
   ka.ws_acc = p.workspace;
   ka.ws_ml = ws ? reinterpret_cast<float2*>(ws + wl.ml) : nullptr;
   ka.n_units = ws ? reinterpret_cast<const int*>(ws + wl.n_units) : nullptr;

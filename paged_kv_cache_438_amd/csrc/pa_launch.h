@@ -57,8 +57,8 @@ struct CacheWriteParams {
   int dtype;
 };
 
-// Byte size of the split-K workspace for these sizes: partials and plan
-// (num_groups > 0 adds the shared-prompt group tables).
+// Byte size of the split-K workspace for these sizes: partials and plan;
+// num_groups >= 0 (shared-prompt decode) adds the group tables, -1 does not.
 size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions,
                               int num_groups);
 

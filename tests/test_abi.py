@@ -102,6 +102,24 @@ def test_splitk_workspace_sizing_and_rejects(lib):
     assert call(flags=4, wsb=small) == 2
 
 
+def test_shared_prefix_workspace_holds_group_tables(lib):
+    """The shared-prompt workspace always holds the group tables the plan
+    writes (group starts, members, prompt lengths), also for zero groups."""
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, d, maxlen, P = 64, 32, 128, 2048, 256
+    parts = maxlen // P + 1                   # one more than the plain split
+    for G in (0, 5):
+        slots = B * H * parts
+        n_units = up(slots * d * 4 + slots * 8)
+        group_fill = up(n_units + 256 + (G + B) * parts * 8)
+        group_start = up(group_fill + G * 4)
+        members = up(group_start + (G + 1) * 4)
+        group_lp = up(members + B * 4)
+        total = up(group_lp + G * 4)
+        assert pa.pa_decode_shared_prefix_workspace_bytes(B, H, d, maxlen, P, G) == total, G
+    assert pa.pa_decode_shared_prefix_workspace_bytes(B, H, d, maxlen, P, -1) == 0
+
+
 def test_check_inputs_host(lib):
     tb = np.array([[3, 1, -1], [0, 2, 5]], dtype=np.int32)
     assert pa.pa_check_inputs_host(tb, [17, 40], 16, 6)[0]

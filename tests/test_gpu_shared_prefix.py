@@ -65,6 +65,13 @@ VARIANTS = [
                   groups=2, group_size=5, num_seqs=10, max_blocks_per_seq=7),
     SMALL.replace(name="shared_small_bs32_d64", block_size=32, head_dim=64, prompt_len=96,
                   length_lo=1, length_hi=70, max_blocks_per_seq=6),
+    # three query heads per KV head and seven members: 21 columns, so one
+    # member's heads straddle two column chunks
+    SMALL.replace(name="shared_small_g3_straddle", num_heads=6, num_kv_heads=2, groups=2,
+                  group_size=7, num_seqs=14),
+    # one head per KV head and 20 members: more members than one chunk holds
+    SMALL.replace(name="shared_small_mha_20", groups=1, group_size=20, num_seqs=20,
+                  length_lo=1, length_hi=9),
 ]
 
 
@@ -131,13 +138,38 @@ def test_shared_prefix_needle_bit_exact():
                 assert got[s, h].tobytes() == exp.tobytes(), (s, h, pos, P)
 
 
-def test_shared_prefix_rerun_bitwise_deterministic():
-    c = make_case(VARIANTS[1])
+@pytest.mark.parametrize("wi", [1, 4, 5])
+def test_shared_prefix_rerun_bitwise_deterministic(wi):
+    """The members of a group are placed by the plan in arrival order and
+    then sorted; reruns must give identical bits, also when members' own
+    tokens are absorbed into the group's last prompt partition (P = 512)."""
+    c = make_case(VARIANTS[wi])
     seq_group, prefix = _groups(c)
     d = DevCase(c)
-    a = host_bits(_run(d, c, seq_group, prefix, 48)).tobytes()
-    b = host_bits(_run(d, c, seq_group, prefix, 48)).tobytes()
-    assert a == b
+    for P in (48, 512):
+        runs = [host_bits(_run(d, c, seq_group, prefix, P)).tobytes() for _ in range(3)]
+        assert runs[0] == runs[1] == runs[2], P
+
+
+def test_shared_prefix_renumbered_sequences():
+    """Renumbering the sequences (same data, rows permuted) changes which
+    column and which token stream of a workgroup serves a member; the output
+    rows still match the oracle, run after run.  (Bits may differ from the
+    unpermuted run: which wave takes which of a member's absorbed steps
+    depends on the other members' lengths before it.)"""
+    c = make_case(VARIANTS[4])
+    seq_group, prefix = _groups(c)
+    perm = np.random.default_rng(3).permutation(c.workload.num_seqs)
+    c2 = make_case(VARIANTS[4])
+    c2.q, c2.block_tables, c2.context_lens = c.q[perm], c.block_tables[perm], c.context_lens[perm]
+    d2 = DevCase(c2)
+    for P in (48, 512):
+        a = host_bits(_run(d2, c2, seq_group[perm], prefix, P))
+        b = host_bits(_run(d2, c2, seq_group[perm], prefix, P))
+        assert a.tobytes() == b.tobytes()
+        got = host_f64(_run(d2, c2, seq_group[perm], prefix, P))
+        torch.cuda.synchronize()
+        _check(got, _oracle(c2), c2.dtype, f"renumbered/P={P}")
 
 
 def test_shared_prefix_contract_violations_give_nan():
@@ -160,6 +192,27 @@ def test_shared_prefix_contract_violations_give_nan():
         _run(d, c, seq_group, prefix, 32, max_group_size=0)
 
 
+def test_shared_prefix_beyond_plan_lds():
+    """4200 sequences in 2100 groups: more sequences and groups than the
+    launch plan stages in LDS, so it reads and writes its tables in global
+    memory; a few sequences are taken out of their groups."""
+    w = SMALL.replace(name="shared_many_groups", num_seqs=4200, groups=2100, group_size=2,
+                      prompt_len=16, length_lo=1, length_hi=8, num_heads=2, num_kv_heads=2,
+                      head_dim=64, max_blocks_per_seq=2)
+    c = make_case(w)
+    seq_group, prefix = _groups(c)
+    seq_group[[5, 777, 4199]] = -1
+    d = DevCase(c)
+    for P in (16, 64):
+        note(f"shared beyond LDS: B=4200 G=2100 P={P}")
+        got = host_f64(_run(d, c, seq_group, prefix, P))
+        torch.cuda.synchronize()
+        _check(got, _oracle(c), w.dtype, f"beyond-LDS/P={P}")
+    # plain split-K over the same 4200 sequences
+    got = host_f64(d.decode("splitk", partition_size=16))
+    _check(got, _oracle(c), w.dtype, "beyond-LDS split-K")
+
+
 def test_full_size_shared_prefix_sampled():
     w = SHARED_PREFIX
     c = make_case(w)
@@ -169,7 +222,7 @@ def test_full_size_shared_prefix_sampled():
     pairs = [(s, int(h)) for s in seqs for h in rng.choice(w.num_heads, size=3, replace=False)]
     ref = _oracle(c, pairs=pairs)
     d = DevCase(c)
-    for P in (256, 1024):
+    for P in (256, 1024, 2048):
         note(f"full shared: P={P} pairs={len(pairs)}")
         got = host_f64(_run(d, c, seq_group, prefix, P))
         torch.cuda.synchronize()
