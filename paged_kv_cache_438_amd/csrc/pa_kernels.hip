@@ -841,7 +841,13 @@ __device__ __forceinline__ int swz_pos(int c, int r) {
 // Dynamic LDS: W * 4 * 16 * D * 2 bytes (two slots of K and V tiles per
 // wave), reused after the loop for the merge of the waves.
 template <int DT, int D, int W, bool BIG_BLOCKS, bool NT>
-__global__ __launch_bounds__(W * 64) void k_decode_mfma(const KArgs a) {
+// Occupancy the register allocation aims at: two waves per SIMD (LDS holds
+// two workgroups per CU anyway); it keeps the kernel in VGPRs only.
+#ifndef PA_MFMA_WPE
+#define PA_MFMA_WPE 2
+#endif
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WPE)))
+void k_decode_mfma(const KArgs a) {
   constexpr int EB = 2;
   constexpr int ROWB = D * EB;
   constexpr int LPR = ROWB / 16;      // lanes (16-byte chunks) per row
@@ -1219,6 +1225,7 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
     s_len[s] = a.lens[s];
     s_grp[s] = shared ? a.seq_group[s] : -1;
   }
+  for (int i = tid; i < NG; i += 1024) glp[i] = a.group_prefix[i];   // checked below
   __syncthreads();
   auto len_of = [&](int s) { return s < kPlanSeqs ? s_len[s] : a.lens[s]; };
   auto grp_of = [&](int s) { return !shared ? -1 : (s < kPlanSeqs ? s_grp[s] : a.seq_group[s]); };
@@ -1246,7 +1253,7 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
       // members than the launch's column chunks cover is out of contract:
       // it is marked invalid (-1), so its members get NaN rows.
       const int cnt = gfill[i];
-      const int lp = a.group_prefix[i];
+      const int lp = glp[i];
       const bool ok = cnt <= pa.max_group_size && lp >= 0 &&
                       lp <= (a.max_blocks << a.bs_log2) &&
                       (lp & ((1 << a.bs_log2) - 1)) == 0 && (lp + P - 1) / P <= a.max_parts;
@@ -1359,49 +1366,52 @@ template <int DT, int D>
 __global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
   constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.num_seqs * a.num_heads || a.n_units[1] == 0) return;
-  const int s = item / a.num_heads;
-  const SeqLayout lay = seq_layout(a, s);
-  if (lay.bad || lay.nparts <= 1) return;   // written by the partition kernel
-  const int np = lay.nparts;
-  const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
-  const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
+  const int total = a.num_seqs * a.num_heads;
+  if (a.n_units[1] == 0) return;       // no sequence has several partitions
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += gridDim.x * 4) {
+    const int s = item / a.num_heads;
+    const SeqLayout lay = seq_layout(a, s);
+    if (lay.bad || lay.nparts <= 1) continue;   // written by the partition kernel
+    const int np = lay.nparts;
+    const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
+    const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
 
-  float M = kEmptyMax;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
-  M = wave_max(M);
-  float lsum = 0.f;
-  for (int p = lane; p < np; p += 64) lsum += ml[p].y * fast_exp2(ml[p].x - M);
-  const float inv = 1.f / wave_sum(lsum);
+    float M = kEmptyMax;
+    for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
+    M = wave_max(M);
+    float lsum = 0.f;
+    for (int p = lane; p < np; p += 64) lsum += ml[p].y * fast_exp2(ml[p].x - M);
+    const float inv = 1.f / wave_sum(lsum);
 
-  float acc[EPL];
+    float acc[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += 64) {
-    const float wl = p0 + lane < np ? fast_exp2(ml[p0 + lane].x - M) : 0.f;
-    const int cnt = min(64, np - p0);
-    auto add = [&](int j) {
-      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                    __builtin_bit_cast(int, wl), j));
-      const float* src = pacc + (size_t)(p0 + j) * D;
-      if constexpr (EPL == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src);
-        acc[0] = fmaf(w, v.x, acc[0]);
-        acc[1] = fmaf(w, v.y, acc[1]);
-      } else {
-        acc[0] = fmaf(w, src[0], acc[0]);
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const float wl = p0 + lane < np ? fast_exp2(ml[p0 + lane].x - M) : 0.f;
+      const int cnt = min(64, np - p0);
+      auto add = [&](int j) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int, wl), j));
+        const float* src = pacc + (size_t)(p0 + j) * D;
+        if constexpr (EPL == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(src);
+          acc[0] = fmaf(w, v.x, acc[0]);
+          acc[1] = fmaf(w, v.y, acc[1]);
+        } else {
+          acc[0] = fmaf(w, src[0], acc[0]);
+        }
+      };
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {     // four independent loads in flight
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) add(j + jj);
       }
-    };
-    int j = 0;
-    for (; j + 4 <= cnt; j += 4) {     // four independent loads in flight
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) add(j + jj);
+      for (; j < cnt; ++j) add(j);
     }
-    for (; j < cnt; ++j) add(j);
-  }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) store_elem<DT>(a.out, (size_t)item * D + lane * EPL + e, acc[e] * inv);
+    for (int e = 0; e < EPL; ++e)
+      store_elem<DT>(a.out, (size_t)item * D + lane * EPL + e, acc[e] * inv);
+  }
 }
 
 struct CArgs {
@@ -1516,6 +1526,10 @@ hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t ld
   else hipLaunchKernelGGL((k_decode_mfma<DT, D, W, false, false>), gd, bd, lds, st, ka);
   return hipGetLastError();
 }
+
+#ifndef PA_REDUCE_MAX_WGS
+#define PA_REDUCE_MAX_WGS 1024
+#endif
 
 // Smallest query-head group sent to the matrix-core kernel.
 #ifndef PA_MFMA_MIN_GROUP
@@ -1667,7 +1681,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     }
   }
   if (e != hipSuccess || ws == nullptr) return e;
-  const int rgrid = (p.num_seqs * p.num_heads + 3) / 4;
+  // One wave per (sequence, head), at most PA_REDUCE_MAX_WGS workgroups of
+  // four waves striding over them.
+  const int rgrid = std::min((p.num_seqs * p.num_heads + 3) / 4, PA_REDUCE_MAX_WGS);
   switch (p.dtype) {
     case kF32: return launch_reduce_t<kF32>(ka, p.head_dim, rgrid, stream);
     case kF16: return launch_reduce_t<kF16>(ka, p.head_dim, rgrid, stream);
