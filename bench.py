@@ -103,6 +103,69 @@ def cpu_baseline(case, min_seconds: float) -> dict:
             "cpu_model": cpu_model, "os_cpu_count": os.cpu_count()}
 
 
+# ----------------------------------------------------------------- block operations
+def block_ops(args) -> dict:
+    """Time pa_copy_blocks and pa_swap_blocks on blocks of the Llama-2-7B
+    shape (32 KV heads x 16 tokens x 128 x fp16 = 128 KiB per block and
+    pool).  Copies: 2048 seeded random (source, destination) pairs in an
+    8192-block pool, bytes = read + write of K and V.  Swaps: 2048 blocks out
+    to a pinned host pool and back in, once as runs of consecutive blocks
+    (one copy per pool and run) and once scattered (one copy per block)."""
+    import torch
+    import paged_kv_cache_438_amd as pa
+    if not pa.LIB_PATH.exists():
+        raise SystemExit("libpa.so is not built: run python __graft_entry__.py build")
+    Hkv, bs, d, NB, NP = 32, 16, 128, 8192, 2048
+    block_bytes = Hkv * bs * d * 2
+    rng = np.random.default_rng(7 if args.seed is None else args.seed)
+    kp = torch.empty((NB, Hkv, bs, d), dtype=torch.float16, device="cuda").normal_()
+    vp = torch.empty_like(kp).normal_()
+    perm = rng.permutation(NB)
+    pairs = np.stack([perm[:NP], perm[NP:2 * NP]], axis=1).astype(np.int32)
+    dpairs = torch.from_numpy(pairs).cuda()
+    hk = torch.empty((NP, Hkv, bs, d), dtype=torch.float16).pin_memory()
+    hv = torch.empty_like(hk).pin_memory()
+    runs = [(int(perm[0] // NP) * NP + i, i) for i in range(NP)]      # consecutive blocks
+    runs = [(g % NB, c) for g, c in runs]
+    scattered = [(int(g), i) for i, g in enumerate(perm[:NP])]
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    reps = max(1, min(args.steps, 20))
+    t_copy = timed(lambda: pa.pa_copy_blocks(kp, vp, dpairs), reps)
+    copy_bytes = 2 * 2 * NP * block_bytes
+    res = {"metric": "block copy / swap throughput", "unit": "GB/s", "n_gpus": 1,
+           "data": "synthetic", "dtype": "f16",
+           "config": {"workload": "llama2_7b blocks", "block_bytes_per_pool": block_bytes,
+                      "pairs": NP, "pool_blocks": NB},
+           "copy_blocks": {"us": round(t_copy * 1e6, 2),
+                           "GBps": round(copy_bytes / t_copy / 1e9, 1),
+                           "frac_of_8TBps": round(copy_bytes / t_copy / 8e12, 4),
+                           "bytes": copy_bytes}}
+    swap_bytes = 2 * NP * block_bytes
+    for name, prs in (("consecutive", runs), ("scattered", scattered)):
+        back = [(c, g) for g, c in prs]
+        t_out = timed(lambda: pa.pa_swap_blocks(hk, hv, kp, vp, prs), max(1, reps // 4))
+        t_in = timed(lambda: pa.pa_swap_blocks(kp, vp, hk, hv, back), max(1, reps // 4))
+        res[f"swap_{name}"] = {"out_us": round(t_out * 1e6, 1),
+                               "out_GBps": round(swap_bytes / t_out / 1e9, 2),
+                               "in_us": round(t_in * 1e6, 1),
+                               "in_GBps": round(swap_bytes / t_in / 1e9, 2),
+                               "bytes": swap_bytes}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # ----------------------------------------------------------------- GPU run
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -124,6 +187,9 @@ def main() -> int:
                     help="plain cached K/V loads (the shared-blocks policy) even without sharing")
     ap.add_argument("--valu-only", action="store_true",
                     help="grouped heads on the vector ALUs instead of the matrix cores")
+    ap.add_argument("--block-ops", action="store_true",
+                    help="instead of decode, time the block copy (copy-on-write) and swap "
+                         "operations on the Llama-2-7B-shaped pool")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run torch copies of this many MiB "
                          "(calibrates HBM byte counters under rocprofv3 --pmc)")
@@ -146,6 +212,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
         return 0
+
+    if args.block_ops:
+        return block_ops(args)
 
     w = WORKLOADS[args.workload]
     entry, P = DEFAULT_ENTRY[w.name]

@@ -1306,25 +1306,33 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
     return (lp + P - 1) / P;
   };
   for (int pass = 0; pass < 2; ++pass) {
-    // pass 0 counts units per size bucket, pass 1 places them
-    auto put = [&](int size, int x, int y) {
+    // pass 0 counts units per size bucket, pass 1 places them.  put() takes
+    // n consecutive partitions y0 .. y0+n-1 of one size with one atomic.
+    auto put = [&](int size, int x, int y0, int n) {
+      if (n <= 0) return;
       const int b = bucket(size);
-      if (pass == 0) atomicAdd(&hist[b], 1);
-      else pa.units[atomicAdd(&hist[b], 1)] = make_int2(x, y);
+      if (pass == 0) {
+        atomicAdd(&hist[b], n);
+      } else {
+        const int at = atomicAdd(&hist[b], n);
+        for (int i = 0; i < n; ++i) pa.units[at + i] = make_int2(x, y0 + i);
+      }
     };
     for (int gi = tid; gi < NG; gi += 1024) {
       const int np = prompt_parts(gi);
-      for (int q = 0; q + 1 < np; ++q) put(P, -(gi + 1), q);
+      put(P, -(gi + 1), 0, np - 1);
       // the last partition: the rest of the prompt plus absorbed own tokens
-      if (np > 0) put(glp[gi] - (np - 1) * P + gfill[gi], -(gi + 1), np - 1);
+      if (np > 0) put(glp[gi] - (np - 1) * P + gfill[gi], -(gi + 1), np - 1, 1);
     }
     for (int s = tid; s < B; s += 1024) {
       const SeqLayout lay = layout(s);
       const int own = lay.nparts - lay.np_pre;
       if (pass == 0 && lay.nparts > 1) atomicAdd(&s_split, 1);
-      if (lay.nparts == 0) put(0, s, 0);
-      for (int q = 0; q < own; ++q)
-        put(min(P, lay.len - lay.lp - q * P), s, lay.np_pre + q);
+      if (lay.nparts == 0) put(0, s, 0, 1);
+      if (own > 0) {
+        put(P, s, lay.np_pre, own - 1);                       // full partitions
+        put(lay.len - lay.lp - (own - 1) * P, s, lay.np_pre + own - 1, 1);
+      }
     }
     __syncthreads();
     if (pass == 0) {
@@ -1456,7 +1464,8 @@ struct BArgs {
 // Copy whole blocks of both pools (every KV head), e.g. the private copy a
 // shared, partly filled block gets before a write.  Workgroup (pair, piece):
 // 256 threads move 16-byte chunks of one block with streaming loads and
-// stores.  Pairs naming a block outside the pool are skipped.
+// stores, four chunks of K and four of V per thread per round, all loaded
+// before any is stored.  Pairs naming a block outside the pool are skipped.
 __global__ __launch_bounds__(256) void k_copy_blocks(const BArgs a) {
   const int pair = blockIdx.y;
   const int src = a.pairs[2 * pair], dst = a.pairs[2 * pair + 1];
@@ -1464,13 +1473,31 @@ __global__ __launch_bounds__(256) void k_copy_blocks(const BArgs a) {
       src == dst)
     return;
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int U = 4;
   const size_t n16 = a.block_bytes / 16;
-  const size_t so = (size_t)src * a.block_bytes, dso = (size_t)dst * a.block_bytes;
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
-    const u32x4 k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.k_pool + so) + i);
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.v_pool + so) + i);
-    __builtin_nontemporal_store(k, reinterpret_cast<u32x4*>(a.k_pool + dso) + i);
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.v_pool + dso) + i);
+  const u32x4* ks = reinterpret_cast<const u32x4*>(a.k_pool + (size_t)src * a.block_bytes);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(a.v_pool + (size_t)src * a.block_bytes);
+  u32x4* kd = reinterpret_cast<u32x4*>(a.k_pool + (size_t)dst * a.block_bytes);
+  u32x4* vd = reinterpret_cast<u32x4*>(a.v_pool + (size_t)dst * a.block_bytes);
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x; i0 < n16; i0 += U * stride) {
+    u32x4 k[U], v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = i0 + u * stride;
+      if (i < n16) {
+        k[u] = __builtin_nontemporal_load(ks + i);
+        v[u] = __builtin_nontemporal_load(vs + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = i0 + u * stride;
+      if (i < n16) {
+        __builtin_nontemporal_store(k[u], kd + i);
+        __builtin_nontemporal_store(v[u], vd + i);
+      }
+    }
   }
 }
 
@@ -1703,6 +1730,7 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, 
   a.block_bytes = block_bytes;
   const size_t chunks = block_bytes / 16;
   const int pieces = (int)std::min<size_t>((chunks + 1023) / 1024, 64);   // 4 chunks per thread
+  // (each thread of a piece then copies one round of four chunks of K and V)
   hipLaunchKernelGGL(k_copy_blocks, dim3(pieces, num_pairs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
