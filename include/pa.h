@@ -263,8 +263,13 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pai
  * (dst_k, dst_v) receives block pairs[i][0] of (src_k, src_v), each block
  * `block_bytes` long.  to_host = 1 copies device -> host, 0 host -> device.
  * `pairs` is a HOST array int32 [num_pairs][2], checked against the pool
- * sizes (PA_ERR_INVALID_ARG).  Runs of consecutive pairs become one copy.
- * Host pools should be pinned for the copies to be asynchronous on `stream`.
+ * sizes (PA_ERR_INVALID_ARG).  Runs of consecutive pairs become one copy per
+ * pool.  When the pairs form more than 8 runs of under 4 MiB each, and the
+ * host pool is pinned memory with a device mapping (hipHostGetDevicePointer
+ * succeeds, as for hipHostMalloc'd memory), one kernel per 256 pairs moves
+ * the blocks through that mapping instead; block_bytes must then be a
+ * multiple of 16 (else the copies are used).  Host pools should be pinned
+ * for either form to be asynchronous on `stream`.
  */
 int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
                    const int32_t* pairs, int num_pairs, int num_dst_blocks, int num_src_blocks,

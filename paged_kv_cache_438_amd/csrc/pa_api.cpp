@@ -332,6 +332,29 @@ int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_
                      pairs[2 * i + 1]);
   const hipMemcpyKind kind = to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (block_bytes % 16 == 0) {
+    // Many short runs: one kernel moves every block through the host pool's
+    // device mapping, when the host pool is pinned memory that has one.
+    int runs = 1;
+    for (int i = 1; i < num_pairs; ++i)
+      runs += !(pairs[2 * i] == pairs[2 * (i - 1)] + 1 &&
+                pairs[2 * i + 1] == pairs[2 * (i - 1) + 1] + 1);
+    if (runs > 8 && (size_t)num_pairs * block_bytes / runs < ((size_t)4 << 20)) {
+      void* host_k = to_host ? dst_k : const_cast<void*>(src_k);
+      void* host_v = to_host ? dst_v : const_cast<void*>(src_v);
+      void* mk = nullptr;
+      void* mv = nullptr;
+      if (hipHostGetDevicePointer(&mk, host_k, 0) == hipSuccess &&
+          hipHostGetDevicePointer(&mv, host_v, 0) == hipSuccess && mk && mv) {
+        const hipError_t e =
+            to_host ? pa::launch_swap_blocks(mk, mv, src_k, src_v, pairs, num_pairs, block_bytes, st)
+                    : pa::launch_swap_blocks(dst_k, dst_v, mk, mv, pairs, num_pairs, block_bytes, st);
+        if (e != hipSuccess) return pa_fail(PA_ERR_HIP, "swap launch failed: %s", hipGetErrorString(e));
+        return pa_ok();
+      }
+      (void)hipGetLastError();   // not mapped: clear the error, copy below
+    }
+  }
   // Runs of pairs whose sources and destinations are both consecutive go out
   // as one copy per pool.
   for (int i = 0; i < num_pairs;) {

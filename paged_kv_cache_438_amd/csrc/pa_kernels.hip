@@ -840,12 +840,12 @@ __device__ __forceinline__ int swz_pos(int c, int r) {
 // partition p); its W waves take the partition's 16-token steps round-robin.
 // Dynamic LDS: W * 4 * 16 * D * 2 bytes (two slots of K and V tiles per
 // wave), reused after the loop for the merge of the waves.
-template <int DT, int D, int W, bool BIG_BLOCKS, bool NT>
 // Occupancy the register allocation aims at: two waves per SIMD (LDS holds
 // two workgroups per CU anyway); it keeps the kernel in VGPRs only.
 #ifndef PA_MFMA_WPE
 #define PA_MFMA_WPE 2
 #endif
+template <int DT, int D, int W, bool BIG_BLOCKS, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WPE)))
 void k_decode_mfma(const KArgs a) {
   constexpr int EB = 2;
@@ -1501,6 +1501,52 @@ __global__ __launch_bounds__(256) void k_copy_blocks(const BArgs a) {
   }
 }
 
+// Move whole blocks between a device pool and a pinned host pool through
+// the host pool's device mapping: workgroup (pair, piece) copies 16-byte
+// chunks of K and V of one block, four of each per thread per round, all
+// loaded before any is stored.  Up to kSwapPairs pairs travel in the kernel
+// arguments (checked on the host).
+constexpr int kSwapPairs = 256;
+struct SArgs {
+  uint8_t* dst_k;
+  uint8_t* dst_v;
+  const uint8_t* src_k;
+  const uint8_t* src_v;
+  size_t block_bytes;     // a multiple of 16
+  int num_pairs;
+  int2 pairs[kSwapPairs]; // (source block, destination block)
+};
+__global__ __launch_bounds__(256) void k_swap_blocks(const SArgs a) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int U = 4;
+  const int2 pr = a.pairs[blockIdx.y];
+  const size_t n16 = a.block_bytes / 16;
+  const u32x4* ks = reinterpret_cast<const u32x4*>(a.src_k + (size_t)pr.x * a.block_bytes);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(a.src_v + (size_t)pr.x * a.block_bytes);
+  u32x4* kd = reinterpret_cast<u32x4*>(a.dst_k + (size_t)pr.y * a.block_bytes);
+  u32x4* vd = reinterpret_cast<u32x4*>(a.dst_v + (size_t)pr.y * a.block_bytes);
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x; i0 < n16; i0 += U * stride) {
+    u32x4 k[U], v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = i0 + u * stride;
+      if (i < n16) {
+        k[u] = __builtin_nontemporal_load(ks + i);
+        v[u] = __builtin_nontemporal_load(vs + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t i = i0 + u * stride;
+      if (i < n16) {
+        __builtin_nontemporal_store(k[u], kd + i);
+        __builtin_nontemporal_store(v[u], vd + i);
+      }
+    }
+  }
+}
+
 int ilog2(int x) {
   int r = 0;
   while ((1 << r) < x) ++r;
@@ -1733,6 +1779,28 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, 
   // (each thread of a piece then copies one round of four chunks of K and V)
   hipLaunchKernelGGL(k_copy_blocks, dim3(pieces, num_pairs), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* pairs, int num_pairs, size_t block_bytes,
+                              hipStream_t stream) {
+  SArgs a;
+  a.dst_k = static_cast<uint8_t*>(dst_k);
+  a.dst_v = static_cast<uint8_t*>(dst_v);
+  a.src_k = static_cast<const uint8_t*>(src_k);
+  a.src_v = static_cast<const uint8_t*>(src_v);
+  a.block_bytes = block_bytes;
+  const size_t chunks = block_bytes / 16;
+  const int pieces = (int)std::min<size_t>((chunks + 1023) / 1024, 64);
+  for (int first = 0; first < num_pairs; first += kSwapPairs) {
+    a.num_pairs = std::min(kSwapPairs, num_pairs - first);
+    for (int i = 0; i < a.num_pairs; ++i)
+      a.pairs[i] = make_int2(pairs[2 * (first + i)], pairs[2 * (first + i) + 1]);
+    hipLaunchKernelGGL(k_swap_blocks, dim3(pieces, a.num_pairs), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {

@@ -63,6 +63,11 @@ size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max
                               int num_groups);
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
+// Block moves between a device pool and a host pool's device mapping; pairs
+// is a host array, already checked against both pools.
+hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                              const int32_t* pairs, int num_pairs, size_t block_bytes,
+                              hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
                               int num_blocks, size_t block_bytes, hipStream_t stream);
 // Single pass when p.workspace == nullptr (then p.max_partitions must be 1).

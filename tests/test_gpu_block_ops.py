@@ -69,6 +69,38 @@ def test_swap_blocks_round_trip():
         pa.pa_swap_blocks(hk, hv, k, v, [(NB, 0)])        # source outside the pool
 
 
+@pytest.mark.parametrize("pinned", [True, False])
+def test_swap_blocks_scattered(pinned):
+    """Forty scattered blocks out and back: with a pinned host pool they move
+    in one kernel through its device mapping, with a pageable one by copies;
+    both must move exactly the named blocks."""
+    rng = np.random.default_rng(8)
+    NB, NC, Hkv, bs, d = 64, 48, 4, 16, 128
+    kp, vp = _pool(rng, NB, Hkv, bs, d, "f16"), _pool(rng, NB, Hkv, bs, d, "f16")
+    k, v = dev_array(kp), dev_array(vp)
+    hk = torch.zeros((NC, Hkv, bs, d), dtype=torch.float16)
+    hv = torch.zeros_like(hk)
+    if pinned:
+        hk, hv = hk.pin_memory(), hv.pin_memory()
+    g = rng.permutation(NB)[:40]
+    c = rng.permutation(NC)[:40]
+    note(f"swap scattered: pinned={pinned} pairs=40")
+    pa.pa_swap_blocks(hk, hv, k, v, list(zip(g.tolist(), c.tolist())))
+    torch.cuda.synchronize()
+    ek = np.zeros((NC, Hkv, bs, d), dtype=np.float16)
+    ev = np.zeros_like(ek)
+    ek[c], ev[c] = kp[g], vp[g]
+    assert hk.numpy().tobytes() == ek.tobytes()
+    assert hv.numpy().tobytes() == ev.tobytes()
+    g2 = rng.permutation(NB)[:40]                          # back into other blocks
+    pa.pa_swap_blocks(k, v, hk, hv, list(zip(c.tolist(), g2.tolist())))
+    torch.cuda.synchronize()
+    fk, fv = kp.copy(), vp.copy()
+    fk[g2], fv[g2] = ek[c], ev[c]
+    assert host_bits(k).tobytes() == fk.tobytes()
+    assert host_bits(v).tobytes() == fv.tobytes()
+
+
 class Mirror:
     """Device pools plus a host copy that receives the same operations."""
 
