@@ -1600,6 +1600,12 @@ hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t ld
   return hipGetLastError();
 }
 
+// Waves per workgroup of the vector kernel for partitions of 512 tokens or
+// more.
+#ifndef PA_SPLIT_WAVES
+#define PA_SPLIT_WAVES 8
+#endif
+
 #ifndef PA_REDUCE_MAX_WGS
 #define PA_REDUCE_MAX_WGS 1024
 #endif
@@ -1720,7 +1726,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   int waves;
   const int row_bytes = p.head_dim * (p.dtype == kF32 ? 4 : 2);
   if (p.workspace == nullptr) waves = gw == 1 && row_bytes <= 256 ? PA_VALU_SINGLE_WAVES : 8;
-  else waves = p.partition_size >= 512 ? 8 : 4;
+  else waves = p.partition_size >= 512 ? PA_SPLIT_WAVES : 4;
   const long long units = p.workspace == nullptr
                               ? p.num_seqs
                               : (long long)(p.num_seqs + (shared ? p.num_groups : 0)) * p.max_partitions;
