@@ -1,0 +1,119 @@
+"""Seeded random sweep of decode configurations on the GPU against the fp64
+oracle.
+
+Each case draws its own shape from a counter-seeded generator: dtype,
+head_dim, KV heads, query heads per KV head (1 to 16, including ones that do
+not divide 16), block size 1 to 256, batch, a length mix with zeros and block
+boundaries, and the entry point (single pass, split-K at one of seven
+partition sizes, the vector-ALU-only flag, or sharing-aware decode over
+random prompt groups).  The case is printed before it runs, so a failure
+names its draw.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_438_amd as pa
+from synthetic import SHARED_PREFIX, TINY, make_case
+from tests.gpu_util import TOL, DevCase, dev_array, host_f64, note
+
+pytestmark = pytest.mark.gpu
+
+N_PLAIN = 60
+N_SHARED = 24
+
+
+def _plain_case(i):
+    rng = np.random.default_rng(70_000 + i)
+    dtype = str(rng.choice(["f32", "f16", "bf16"]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    bs = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256]))
+    B = int(rng.integers(1, 10))
+    cap = int(rng.choice([20, 100, 400, 900]))
+    lens = rng.integers(0, cap + 1, size=B)
+    specials = [0, 1, bs, bs + 1, max(bs - 1, 1), cap]
+    for j in range(B):
+        if rng.random() < 0.3:
+            lens[j] = min(int(rng.choice(specials)), cap)
+    mb = max(1, -(-int(lens.max()) // bs)) + int(rng.integers(0, 3))
+    used = int(sum(-(-int(L) // bs) for L in lens))
+    entry = str(rng.choice(["single", "splitk", "single_valu", "splitk_valu"]))
+    P = int(rng.choice([16, 32, 48, 64, 128, 256, 512]))
+    w = TINY.replace(name=f"sweep{i}", num_seqs=B, num_heads=hkv * G, num_kv_heads=hkv,
+                     head_dim=d, block_size=bs, dtype=dtype, seed=80_000 + i,
+                     length_kind="fixed", lengths=tuple(int(x) for x in lens),
+                     num_blocks=2 * used + 3, max_blocks_per_seq=mb)
+    return w, entry, P
+
+
+def _shared_case(i):
+    rng = np.random.default_rng(90_000 + i)
+    dtype = str(rng.choice(["f16", "bf16"]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 3, 4, 8]))
+    bs = int(rng.choice([1, 4, 16, 32, 64]))
+    groups = int(rng.integers(1, 4))
+    gsize = int(rng.integers(1, 9))
+    prompt = bs * int(rng.integers(1, max(2, 200 // bs)))
+    lo = int(rng.integers(1, 40))
+    hi = lo + int(rng.integers(0, 200))
+    P = int(rng.choice([16, 48, 64, 256, 512, 2048]))
+    mb = -(-(prompt + hi) // bs) + int(rng.integers(0, 2))
+    w = SHARED_PREFIX.replace(name=f"sweep_shared{i}", num_seqs=groups * gsize,
+                              num_heads=hkv * G, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                              dtype=dtype, seed=95_000 + i, groups=groups, group_size=gsize,
+                              prompt_len=prompt, length_lo=lo, length_hi=hi,
+                              max_blocks_per_seq=mb)
+    return w, P
+
+
+def _check(got, ref, dtype, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    note(f"  {what}: max|err| = {err:.3e} (bound {TOL[dtype]:.0e})")
+    assert err <= TOL[dtype], f"{what}: max abs error {err} > {TOL[dtype]}"
+
+
+@pytest.mark.parametrize("i", range(N_PLAIN))
+def test_random_decode_matches_oracle(i):
+    w, entry, P = _plain_case(i)
+    c = make_case(w)
+    note(f"sweep {i}: {w.dtype} d={w.head_dim} Hq={w.num_heads} Hkv={w.num_kv_heads} "
+         f"bs={w.block_size} lens={list(w.lengths)} MB={w.max_blocks_per_seq} "
+         f"entry={entry} P={P}")
+    d = DevCase(c)
+    valu = entry.endswith("_valu")
+    got = host_f64(d.decode(entry.split("_")[0], partition_size=P, valu_only=valu))
+    torch.cuda.synchronize()
+    ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
+                        c.block_size, c.dtype)
+    _check(got, ref, w.dtype, f"sweep {i}")
+
+
+@pytest.mark.parametrize("i", range(N_SHARED))
+def test_random_shared_prefix_matches_oracle(i):
+    w, P = _shared_case(i)
+    c = make_case(w)
+    B = w.num_seqs
+    seq_group = np.full(B, -1, dtype=np.int32)
+    for gi, members in enumerate(c.shared_groups):
+        seq_group[members] = gi
+    prefix = np.full(len(c.shared_groups), w.prompt_len, dtype=np.int32)
+    mg = int(c.shared_groups.shape[1])
+    note(f"sweep shared {i}: {w.dtype} d={w.head_dim} Hq={w.num_heads} Hkv={w.num_kv_heads} "
+         f"bs={w.block_size} groups={w.groups}x{w.group_size} prompt={w.prompt_len} "
+         f"lens={c.context_lens.tolist()} P={P}")
+    d = DevCase(c)
+    got = host_f64(pa.pa_decode_shared_prefix(d.q, d.k_pool, d.v_pool, d.tables, d.lens,
+                                              dev_array(seq_group), dev_array(prefix), mg, P,
+                                              int(c.context_lens.max()), scale=float(c.scale)))
+    torch.cuda.synchronize()
+    ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
+                        c.block_size, c.dtype)
+    _check(got, ref, w.dtype, f"sweep shared {i}")
