@@ -103,6 +103,19 @@ def cpu_baseline(case, min_seconds: float) -> dict:
             "cpu_model": cpu_model, "os_cpu_count": os.cpu_count()}
 
 
+# ----------------------------------------------------------------- traffic records
+def kernel_code_digest() -> str:
+    """sha256 of the kernel source with comments and blank lines removed and
+    whitespace collapsed: HBM counters recorded for one digest stay valid
+    across comment edits, and are dropped once the code changes."""
+    import hashlib
+    import re
+    src = (ROOT / "paged_kv_cache_438_amd" / "csrc" / "pa_kernels.hip").read_text()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    lines = [" ".join(re.sub(r"//.*", "", l).split()) for l in src.splitlines()]
+    return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()
+
+
 # ----------------------------------------------------------------- block operations
 def block_ops(args) -> dict:
     """Time pa_copy_blocks and pa_swap_blocks on blocks of the Llama-2-7B
@@ -335,9 +348,7 @@ def main() -> int:
     if tf.exists():
         try:
             rec = json.loads(tf.read_text())
-            import hashlib
-            src = (ROOT / "paged_kv_cache_438_amd" / "csrc" / "pa_kernels.hip").read_bytes()
-            if rec.get("kernel_source_sha256") == hashlib.sha256(src).hexdigest():
+            if rec.get("kernel_code_sha256") == kernel_code_digest():
                 traffic = rec.get("hbm_bytes_per_launch")
         except Exception:
             traffic = None

@@ -36,6 +36,23 @@
 // sequence's length or table entries past its last block) and its scores are
 // set to -inf, giving exactly zero weight.  Lengths or block ids outside the
 // documented contract make the output NaN instead of faulting.
+//
+// Kernels in this file
+// --------------------
+// k_decode       the vector-ALU decode described above (MHA, fp32, and
+//                grouped heads under the VALU-only flag).
+// k_decode_mfma  grouped heads on the matrix cores: S^T = K Q^T and
+//                O^T = V^T P^T per 16-token step, K/V staged in LDS by
+//                direct-to-LDS loads; also every shared-prompt unit, whose
+//                columns are the queries of all members of a group.
+// k_plan         one workgroup per split call: orders the (sequence or
+//                group, partition) units longest first and, for shared
+//                prompts, builds the group tables.
+// k_reduce       merges a split sequence's partitions in fixed order.
+// k_cache_write  the new token's K/V into its slot.
+// k_copy_blocks  whole-block copies inside the pools (copy-on-write).
+// k_swap_blocks  whole-block moves between the device pools and a pinned
+//                host pool through its device mapping.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
