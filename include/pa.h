@@ -148,9 +148,10 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
  * Bytes of device workspace pa_decode_splitk needs for these sizes: fp32
  * partial results for num_seqs * num_heads * ceil(max_context_len /
  * partition_size) partitions, each head_dim accumulators plus a running
- * maximum and sum, then the launch plan (one 8-byte entry per possible
- * (sequence, partition) pair plus 256 bytes), each part rounded up to 256
- * bytes.  Returns 0 for invalid sizes.
+ * maximum and sum, then the launch plan (256 bytes of counts, one 8-byte
+ * entry per possible (sequence, partition) pair, and 4 bytes per sequence
+ * for the list of sequences with several partitions), each part rounded up
+ * to 256 bytes.  Returns 0 for invalid sizes.
  */
 size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim,
                                         int max_context_len, int partition_size);
@@ -163,9 +164,10 @@ size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_di
  * partition launch takes them in that order and computes, per (sequence,
  * head, partition), the partition's maximum score m, sum of exp(score - m)
  * and unnormalised weighted value sum into `workspace`; the last launch
- * merges the partitions of each (sequence, head) in fixed order, rescaling
- * each by exp(m_p - max_p m_p), and writes `out`.  Sequences with a single
- * partition are written directly by the partition launch.  The result does
+ * merges the partitions of each (sequence, head) of the sequences the plan
+ * listed as split, in fixed order, rescaling each by exp(m_p - max_p m_p),
+ * and writes `out`.  Sequences with a single partition are written directly
+ * by the partition launch.  The result does
  * not depend on the order in which partitions run.
  *
  * max_context_len is a host-known bound on every context_lens[s] (no device

@@ -225,6 +225,7 @@ struct KArgs {
   const int* n_units;   // split-K plan: number of (sequence, partition) units,
                         // then the number of sequences with several partitions
   const int2* units;    // split-K plan: units, longest first
+  const int* split;     // split-K plan: the sequences with several partitions
   // Shared-prompt decode (nullptr otherwise): the group of each sequence
   // (-1: none), each group's shared prompt length, and the members of each
   // group (members[group_start[i] .. group_start[i+1]) ).
@@ -1170,6 +1171,7 @@ struct PArgs {
   KArgs k;              // sizes, lengths and (shared-prompt decode) the caller's groups
   int* n_units;
   int2* units;          // [(num_groups + num_seqs) * max_parts]
+  int* split;           // [num_seqs]: sequences with several partitions (n_units[1] of them)
   int* group_fill;      // [num_groups] scratch
   int* group_start;     // [num_groups + 1]
   int* members;         // [num_seqs]
@@ -1344,7 +1346,7 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
     for (int s = tid; s < B; s += 1024) {
       const SeqLayout lay = layout(s);
       const int own = lay.nparts - lay.np_pre;
-      if (pass == 0 && lay.nparts > 1) atomicAdd(&s_split, 1);
+      if (pass == 0 && lay.nparts > 1) pa.split[atomicAdd(&s_split, 1)] = s;
       if (lay.nparts == 0) put(0, s, 0, 1);
       if (own > 0) {
         put(P, s, lay.np_pre, own - 1);                       // full partitions
@@ -1381,22 +1383,24 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave per (sequence, head) merges the partitions of a split sequence:
-// with M = max_p m_p, out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
+// One wave per (sequence, head) of the sequences the plan listed as split
+// merges their partitions: with M = max_p m_p,
+//   out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
 // Lanes first read the (m, l) pairs of 64 partitions at a time, then every
 // lane accumulates its head-dim elements over the partitions in order
-// p = 0, 1, ..., taking each weight from the lane that computed it.  All
-// sums run in a fixed order, so reruns give identical bits.
+// p = 0, 1, ..., taking each weight from the lane that computed it, with
+// eight loads in flight.  All sums run in a fixed order, so reruns give
+// identical bits (the order of the list does not matter).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
   constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
+  constexpr int U = 8;                 // partition loads in flight
   const int lane = threadIdx.x & 63;
-  const int total = a.num_seqs * a.num_heads;
-  if (a.n_units[1] == 0) return;       // no sequence has several partitions
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += gridDim.x * 4) {
-    const int s = item / a.num_heads;
+  const int total = a.n_units[1] * a.num_heads;
+  for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < total; it += gridDim.x * 4) {
+    const int s = a.split[it / a.num_heads];
+    const int item = s * a.num_heads + it % a.num_heads;
     const SeqLayout lay = seq_layout(a, s);
-    if (lay.bad || lay.nparts <= 1) continue;   // written by the partition kernel
     const int np = lay.nparts;
     const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
     const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
@@ -1414,24 +1418,36 @@ __global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
     for (int p0 = 0; p0 < np; p0 += 64) {
       const float wl = p0 + lane < np ? fast_exp2(ml[p0 + lane].x - M) : 0.f;
       const int cnt = min(64, np - p0);
-      auto add = [&](int j) {
+      auto add = [&](int j, const float* v) {
         const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                       __builtin_bit_cast(int, wl), j));
-        const float* src = pacc + (size_t)(p0 + j) * D;
-        if constexpr (EPL == 2) {
-          const float2 v = *reinterpret_cast<const float2*>(src);
-          acc[0] = fmaf(w, v.x, acc[0]);
-          acc[1] = fmaf(w, v.y, acc[1]);
-        } else {
-          acc[0] = fmaf(w, src[0], acc[0]);
-        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, v[e], acc[e]);
       };
       int j = 0;
-      for (; j + 4 <= cnt; j += 4) {     // four independent loads in flight
+      for (; j + U <= cnt; j += U) {
+        float v[U][EPL];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) add(j + jj);
+        for (int u = 0; u < U; ++u) {
+          const float* src = pacc + (size_t)(p0 + j + u) * D;
+          if constexpr (EPL == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(src);
+            v[u][0] = t.x;
+            v[u][1] = t.y;
+          } else {
+            v[u][0] = src[0];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(j + u, v[u]);
       }
-      for (; j < cnt; ++j) add(j);
+      for (; j < cnt; ++j) {
+        float v[EPL];
+        const float* src = pacc + (size_t)(p0 + j) * D;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[e] = src[e];
+        add(j, v);
+      }
     }
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
@@ -1660,11 +1676,12 @@ hipError_t launch_reduce_t(const KArgs& ka, int d, int grid, hipStream_t st) {
 
 // Split-K workspace, each part starting on a 256-byte boundary:
 //   acc   [B][Hq][Pmax][D] fp32 and (m, l) [B][Hq][Pmax]
-//   plan  unit count (256 bytes), units [(G + B) * Pmax] of (x, y)
+//   plan  unit count and split count (256 bytes), units [(G + B) * Pmax] of
+//         (x, y), split sequences [B]
 //   with prompt groups: group_fill [G], group_start [G + 1], members [B],
 //   group_lp [G].
 struct WsLayout {
-  size_t ml, n_units, units, group_fill, group_start, members, group_lp, total;
+  size_t ml, n_units, units, split, group_fill, group_start, members, group_lp, total;
 };
 static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 // num_groups < 0: a plain split-K call, no group tables.
@@ -1677,7 +1694,8 @@ static WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_par
   w.ml = slots * head_dim * sizeof(float);
   w.n_units = up256(w.ml + slots * sizeof(float2));
   w.units = w.n_units + 256;
-  w.group_fill = up256(w.units + (size_t)(num_groups + num_seqs) * max_partitions * sizeof(int2));
+  w.split = up256(w.units + (size_t)(num_groups + num_seqs) * max_partitions * sizeof(int2));
+  w.group_fill = up256(w.split + (size_t)num_seqs * sizeof(int));
   w.group_start = up256(w.group_fill + (size_t)num_groups * sizeof(int));
   w.members = up256(w.group_start + (size_t)(num_groups + 1) * sizeof(int));
   w.group_lp = up256(w.members + (size_t)num_seqs * sizeof(int));
@@ -1708,6 +1726,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.ws_ml = ws ? reinterpret_cast<float2*>(ws + wl.ml) : nullptr;
   ka.n_units = ws ? reinterpret_cast<const int*>(ws + wl.n_units) : nullptr;
   ka.units = ws ? reinterpret_cast<const int2*>(ws + wl.units) : nullptr;
+  ka.split = ws ? reinterpret_cast<const int*>(ws + wl.split) : nullptr;
   // The partition and reduce launches read the plan's copies of the groups.
   ka.seq_group = shared ? p.seq_group : nullptr;
   ka.group_prefix = shared ? reinterpret_cast<const int32_t*>(ws + wl.group_lp) : nullptr;
@@ -1757,6 +1776,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     pa_.k.group_prefix = p.group_prefix;       // the caller's prompt lengths
     pa_.n_units = reinterpret_cast<int*>(ws + wl.n_units);
     pa_.units = reinterpret_cast<int2*>(ws + wl.units);
+    pa_.split = reinterpret_cast<int*>(ws + wl.split);
     pa_.group_fill = shared ? reinterpret_cast<int*>(ws + wl.group_fill) : nullptr;
     pa_.group_start = shared ? reinterpret_cast<int*>(ws + wl.group_start) : nullptr;
     pa_.members = shared ? reinterpret_cast<int*>(ws + wl.members) : nullptr;
@@ -1777,8 +1797,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     }
   }
   if (e != hipSuccess || ws == nullptr) return e;
-  // One wave per (sequence, head), at most PA_REDUCE_MAX_WGS workgroups of
-  // four waves striding over them.
+  // One wave per (split sequence, head), at most PA_REDUCE_MAX_WGS
+  // workgroups of four waves striding over them (the count is on the device).
   const int rgrid = std::min((p.num_seqs * p.num_heads + 3) / 4, PA_REDUCE_MAX_WGS);
   switch (p.dtype) {
     case kF32: return launch_reduce_t<kF32>(ka, p.head_dim, rgrid, stream);

@@ -80,9 +80,11 @@ def test_cache_write_rejects(lib):
 
 def test_splitk_workspace_sizing_and_rejects(lib):
     need = pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 256)
-    partials = ((64 * 32 * 8 * (128 + 2) * 4) + 255) // 256 * 256
-    plan = 256 + 64 * 8 * 8                  # unit count, then one (seq, part) pair each
-    assert need == (partials + plan + 255) // 256 * 256
+    up = lambda x: (x + 255) // 256 * 256
+    partials = up(64 * 32 * 8 * (128 + 2) * 4)
+    plan = up(256 + 64 * 8 * 8)              # counts, then one (seq, part) pair each
+    split = up(64 * 4)                       # the sequences with several partitions
+    assert need == partials + plan + split
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 24) == 0
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 96, 2048, 256) == 0
 
@@ -111,7 +113,8 @@ def test_shared_prefix_workspace_holds_group_tables(lib):
     for G in (0, 5):
         slots = B * H * parts
         n_units = up(slots * d * 4 + slots * 8)
-        group_fill = up(n_units + 256 + (G + B) * parts * 8)
+        split = up(n_units + 256 + (G + B) * parts * 8)
+        group_fill = up(split + B * 4)
         group_start = up(group_fill + G * 4)
         members = up(group_start + (G + 1) * 4)
         group_lp = up(members + B * 4)
