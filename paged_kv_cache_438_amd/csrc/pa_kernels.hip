@@ -836,6 +836,27 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lgkmcnt0() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
+// An empty asm that the compiler sees as rewriting the registers of operands
+// read from LDS by assembly.  The compiler takes an asm output as ready when
+// the asm ends; placed after the wait for those reads, this keeps every use,
+// copy or spill of the operands below the wait.
+template <int N>
+__device__ __forceinline__ void tie_operands(uint4 (&b)[N]);
+template <>
+__device__ __forceinline__ void tie_operands<4>(uint4 (&b)[4]) {
+  asm volatile(""
+               : "+v"(b[0].x), "+v"(b[0].y), "+v"(b[0].z), "+v"(b[0].w),
+                 "+v"(b[1].x), "+v"(b[1].y), "+v"(b[1].z), "+v"(b[1].w),
+                 "+v"(b[2].x), "+v"(b[2].y), "+v"(b[2].z), "+v"(b[2].w),
+                 "+v"(b[3].x), "+v"(b[3].y), "+v"(b[3].z), "+v"(b[3].w));
+}
+template <>
+__device__ __forceinline__ void tie_operands<2>(uint4 (&b)[2]) {
+  asm volatile(""
+               : "+v"(b[0].x), "+v"(b[0].y), "+v"(b[0].z), "+v"(b[0].w),
+                 "+v"(b[1].x), "+v"(b[1].y), "+v"(b[1].z), "+v"(b[1].w));
+}
+
 template <bool NT>
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
   // aux bit 1 = slc: the streaming (non-temporal) policy of ld16_stream
@@ -1099,9 +1120,11 @@ void k_decode_mfma(const KArgs a) {
     const int slot = k & 1;
     if (k + 1 < nk) wait_vmcnt<2 * NDMA>();   // the younger slot may stay in flight
     else wait_vmcnt<0>();
-    const Ops ops = read_ops(slot);
-    wait_lgkmcnt0();
+    Ops ops = read_ops(slot);
+    wait_lgkmcnt0();                          // the slot is read: it may be refilled
     if (k + 2 < nk) issue(k + 2, slot);
+    tie_operands(ops.k);                      // uses of the operands stay below the wait
+    tie_operands(ops.v);
     compute_step(k, ops);
   }
 
