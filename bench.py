@@ -212,7 +212,7 @@ def main() -> int:
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
               f"{world}): paged decode shards by sequence or KV head with no exchange inside "
-              "attention, and this build measures the single-GPU kernel.", flush=True)
+              "attention, and this benchmark measures the single-GPU kernel.", flush=True)
         return 2
 
     if args.copy_probe_mib:

@@ -1,0 +1,54 @@
+"""The benchmark's contract: one JSON line with the metric, the timing, the
+roofline record and the baseline fields (GPU), and a plain refusal for more
+than one GPU (CPU)."""
+from __future__ import annotations
+
+import json
+import pathlib
+import subprocess
+import sys
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+
+
+def _bench(*args, timeout=300):
+    return subprocess.run([sys.executable, str(ROOT / "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=timeout)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("args", [("--workload", "tiny"),
+                                  ("--workload", "tiny", "--entry", "splitk", "--partition", "16")])
+def test_bench_prints_one_json_line(args):
+    r = _bench(*args, "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    rec = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in rec, key
+    assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
+    assert rec["value"] > 0 and rec["ms_per_step"] > 0
+    assert rec["config"]["workload"] == "tiny"
+    rf = rec["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert rf["achieved"] > 0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+
+
+@pytest.mark.gpu
+def test_block_ops_mode_prints_one_json_line():
+    r = _bench("--block-ops", "--steps", "2")
+    assert r.returncode == 0, r.stderr[-2000:]
+    rec = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    assert rec["copy_blocks"]["GBps"] > 0
+    assert rec["swap_consecutive"]["out_GBps"] > 0 and rec["swap_scattered"]["in_GBps"] > 0
