@@ -863,6 +863,21 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, NT ? 2 : 0);
 }
 
+// The same 16-byte load to LDS through a buffer resource: `rsrc` covers one
+// (block, KV head) tile, `off` is the byte offset inside it (out-of-range
+// offsets read zeros instead of faulting).
+#ifndef PA_MFMA_BUFFER_LDS
+#define PA_MFMA_BUFFER_LDS 1
+#endif
+template <bool NT>
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, int off, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, NT ? 2 : 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+
 // Block tables are read-only for the whole kernel: reading them through the
 // constant address space lets wave-uniform lookups stay scalar loads even
 // though the inline assembly above is marked as touching memory.
@@ -1013,16 +1028,33 @@ void k_decode_mfma(const KArgs a) {
     for (int i = 0; i < (BIG_BLOCKS ? 1 : NDMA); ++i) ids.cur[i] = ids.nxt[i];
     fetch_ids(k + 1 < nk ? k + 1 : k);
     uint8_t* dst = wave_lds + slot * SLOT;
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j) {
-      const int row = j * RPI + lrow;
-      const int t = min(t0 + row, t_end - 1);
-      int ph = ids.cur[BIG_BLOCKS ? 0 : j];
+    if constexpr (BIG_BLOCKS && PA_MFMA_BUFFER_LDS) {
+      // One block per step: buffer resources over its K and V tiles.
+      int ph = ids.cur[0];
       if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
-      const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
-                         (size_t)(t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
-      dma16<NT>(a.k_pool + off, dst + j * 1024);
-      dma16<NT>(a.v_pool + off, dst + TILE + j * 1024);
+      const size_t tile = (size_t)ph * block_bytes + (size_t)g * tile_bytes;
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k_pool + tile, (int)tile_bytes);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v_pool + tile, (int)tile_bytes);
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int row = j * RPI + lrow;
+        const int t = min(t0 + row, t_end - 1);
+        const int off = (t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
+        dma16_buf<NT>(rk, off, dst + j * 1024);
+        dma16_buf<NT>(rv, off, dst + TILE + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int row = j * RPI + lrow;
+        const int t = min(t0 + row, t_end - 1);
+        int ph = ids.cur[BIG_BLOCKS ? 0 : j];
+        if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
+        const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
+                           (size_t)(t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
+        dma16<NT>(a.k_pool + off, dst + j * 1024);
+        dma16<NT>(a.v_pool + off, dst + TILE + j * 1024);
+      }
     }
   };
   struct Ops { uint4 k[NI], v[NI]; };
