@@ -33,7 +33,7 @@ METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and KV tokens/se
 # partitions, the best trade between balance and per-partition overhead for
 # its log-normal length mix (lengths up to 16384).
 DEFAULT_ENTRY = {"llama2_7b": ("single", None), "long_bs512": ("splitk", 512),
-                 "gqa_70b": ("splitk", 4096), "shared_prefix": ("shared", 2048),
+                 "gqa_70b": ("splitk", 8192), "shared_prefix": ("shared", 2048),
                  "tiny": ("single", None)}
 ENTRY_NAME = {"single": "pa_decode", "splitk": "pa_decode_splitk",
               "shared": "pa_decode_shared_prefix"}
