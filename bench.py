@@ -179,6 +179,32 @@ def block_ops(args) -> dict:
     return 0
 
 
+def read_ceiling(pa, torch, seed: int = 5) -> dict:
+    """The read rate a decode kernel can approach on this GPU: pa_read_probe
+    over a 1 GiB buffer in 4 KiB tiles (the size of one (block, head) tile at
+    block_size 16, head_dim 128, 2-byte elements), read in order and in a
+    seeded random order, 10 launches each, timed with HIP events."""
+    tile, n = 4096, (1 << 30) // 4096
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {"kind": "pa_read_probe, 1 GiB in 4 KiB tiles, non-temporal 16-byte loads"}
+    orders = {"sequential": np.arange(n, dtype=np.int32),
+              "random_tiles": np.random.default_rng(seed).permutation(n).astype(np.int32)}
+    for name, order in orders.items():
+        o = torch.from_numpy(order).cuda()
+        for _ in range(3):
+            pa.pa_read_probe(buf, tile, o, sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            pa.pa_read_probe(buf, tile, o, sink)
+        b.record()
+        torch.cuda.synchronize()
+        res[name + "_GBps"] = round(n * tile / (a.elapsed_time(b) / 10 * 1e-3) / 1e9, 1)
+    del buf
+    return res
+
+
 # ----------------------------------------------------------------- GPU run
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -200,6 +226,8 @@ def main() -> int:
                     help="plain cached K/V loads (the shared-blocks policy) even without sharing")
     ap.add_argument("--valu-only", action="store_true",
                     help="grouped heads on the vector ALUs instead of the matrix cores")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the read-probe measurement reported beside the roofline")
     ap.add_argument("--block-ops", action="store_true",
                     help="instead of decode, time the block copy (copy-on-write) and swap "
                          "operations on the Llama-2-7B-shaped pool")
@@ -343,6 +371,10 @@ def main() -> int:
     tokens = kv_token_count(case)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
+    ceiling = read_ceiling(pa, torch) if not args.no_read_ceiling else None
+    if ceiling:
+        ceiling["decode_frac_of_random_tiles"] = round(achieved / ceiling["random_tiles_GBps"], 4)
+
     traffic = None
     tf = ROOT / "profiles" / f"traffic_{w.name}_{entry}.json"
     if tf.exists():
@@ -385,6 +417,7 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": dec_bytes,
                      "logical_bytes_per_launch": logical_bytes},
         "cpu_baseline": cpu,
+        "read_ceiling": ceiling,
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -278,6 +278,21 @@ int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_
                    size_t block_bytes, int to_host, void* stream);
 
 /*
+ * pa_read_probe -- a measurement aid, not part of decode: reads num_tiles
+ * tiles of tile_bytes bytes (a positive multiple of 4096) of the DEVICE
+ * buffer `buf`, tile tile_order[i] at byte offset tile_order[i] * tile_bytes,
+ * with the 16-byte non-temporal loads the decode kernels use, and writes
+ * nothing (`sink`, a DEVICE uint32, is written only for one value the data
+ * never produces).  tile_order (DEVICE int32 [num_tiles]) must name tiles
+ * inside the buffer.  With an identity order it measures a sequential read;
+ * with a random permutation of 4 KiB tiles, the scattered (block, head)
+ * tiles of a paged pool: the read ceiling a decode kernel can approach on
+ * this GPU.  Asynchronous on `stream`.
+ */
+int pa_read_probe(const void* buf, size_t tile_bytes, const int32_t* tile_order, int num_tiles,
+                  uint32_t* sink, void* stream);
+
+/*
  * pa_check_inputs_host -- validate HOST copies of the device data against the
  * contract above: 0 <= L <= max_blocks_per_seq * block_size, every table entry
  * in use in [0, num_blocks), and, if check_write_targets is nonzero, that no

@@ -32,6 +32,7 @@ _SIGNATURES = {
     "pa_decode_splitk": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
                          [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
                           _c_void_p]),
+    "pa_read_probe": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p, _c_void_p]),
     "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
                              [ctypes.POINTER(_c_int)]),
     "pa_decode_shared_prefix_workspace_bytes": (_c_size_t, [_c_int] * 6),
@@ -315,6 +316,23 @@ def pa_swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor
                                src_v.data_ptr(), pr.ctypes.data, pr.shape[0], dst_k.shape[0],
                                src_k.shape[0], block_bytes, to_host, _stream(dev, stream))
     _check(st, "pa_swap_blocks")
+
+
+def pa_read_probe(buf: torch.Tensor, tile_bytes: int, tile_order: torch.Tensor,
+                  sink: torch.Tensor, stream=None) -> None:
+    """Read the tiles of ``buf`` named by ``tile_order`` (int32, device) with
+    the decode kernels' loads; a measurement aid (see include/pa.h)."""
+    _dev(buf, "buf")
+    _dev(tile_order, "tile_order")
+    _dev(sink, "sink")
+    if tile_order.dtype != torch.int32 or tile_order.dim() != 1:
+        raise TypeError("tile_order must be a 1-D int32 tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if tile_bytes <= 0 or tile_bytes % 4096 or nbytes < tile_bytes:
+        raise ValueError("tile_bytes must be a positive multiple of 4096 within the buffer")
+    st = load().pa_read_probe(buf.data_ptr(), tile_bytes, tile_order.data_ptr(),
+                              tile_order.numel(), sink.data_ptr(), _stream(buf.device, stream))
+    _check(st, "pa_read_probe")
 
 
 def pa_check_inputs_host(block_tables, context_lens, block_size: int, num_blocks: int,

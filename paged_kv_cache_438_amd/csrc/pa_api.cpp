@@ -375,6 +375,18 @@ int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_
   return pa_ok();
 }
 
+int pa_read_probe(const void* buf, size_t tile_bytes, const int32_t* tile_order, int num_tiles,
+                  uint32_t* sink, void* stream) {
+  if (num_tiles < 0 || tile_bytes == 0 || tile_bytes % 4096 != 0)
+    return pa_fail(PA_ERR_INVALID_ARG, "tile_bytes must be a positive multiple of 4096 and "
+                                       "num_tiles >= 0");
+  if (num_tiles == 0) return pa_ok();
+  if (!buf || !tile_order || !sink) return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(buf)) return pa_fail(PA_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+  return finish_launch(pa::launch_read_probe(buf, tile_bytes, tile_order, num_tiles, sink,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int pa_check_inputs_host(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                          int block_size, int max_blocks_per_seq, int num_blocks,
                          int check_write_targets, int* bad_seq) {

@@ -68,6 +68,8 @@ hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream);
 hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
                               const int32_t* pairs, int num_pairs, size_t block_bytes,
                               hipStream_t stream);
+hipError_t launch_read_probe(const void* buf, size_t tile_bytes, const int32_t* order,
+                             int ntiles, uint32_t* sink, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
                               int num_blocks, size_t block_bytes, hipStream_t stream);
 // Single pass when p.workspace == nullptr (then p.max_partitions must be 1).

@@ -78,6 +78,14 @@ def test_cache_write_rejects(lib):
     assert lib.pa_cache_write(*bad) == 2
 
 
+def test_read_probe_rejects(lib):
+    assert lib.pa_read_probe(P, 1000, P, 4, P, None) == 2          # not a multiple of 4096
+    assert lib.pa_read_probe(P, 4096, P, -1, P, None) == 2
+    assert lib.pa_read_probe(0, 4096, P, 4, P, None) == 1
+    assert lib.pa_read_probe(P + 8, 4096, P, 4, P, None) == 2      # misaligned buffer
+    assert lib.pa_read_probe(0, 4096, 0, 0, 0, None) == 0          # nothing to read
+
+
 def test_splitk_workspace_sizing_and_rejects(lib):
     need = pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 256)
     up = lambda x: (x + 255) // 256 * 256
