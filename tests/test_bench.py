@@ -52,3 +52,22 @@ def test_block_ops_mode_prints_one_json_line():
     rec = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
     assert rec["copy_blocks"]["GBps"] > 0
     assert rec["swap_consecutive"]["out_GBps"] > 0 and rec["swap_scattered"]["in_GBps"] > 0
+
+
+def test_cpu_baseline_record_on_the_tiny_workload():
+    """The oracle's timing record: pool rate, worker count and the
+    single-process rate, on whole passes of the workload."""
+    import importlib.util
+    sys.path.insert(0, str(ROOT))
+    from synthetic import TINY, kv_token_count, make_case
+    spec = importlib.util.spec_from_file_location("bench_mod", ROOT / "bench.py")
+    bench = importlib.util.module_from_spec(spec)
+    sys.modules["bench_mod"] = bench          # the fork pool pickles its worker by name
+    spec.loader.exec_module(bench)
+    case = make_case(TINY)
+    rec = bench.cpu_baseline(case, 0.2)
+    assert rec["kind"] == "oracle" and rec["unit"] == "KV tokens/s"
+    assert rec["value"] > 0 and 1 <= rec["cores"] <= 16
+    assert str(kv_token_count(case)) in rec["sample"]
+    one = rec["one_worker"]
+    assert one["cores"] == 1 and one["value"] > 0
