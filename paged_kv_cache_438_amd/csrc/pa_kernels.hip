@@ -383,16 +383,32 @@ __device__ __forceinline__ Col column_of(const KArgs& a, const KUnit& u, const S
   return c;
 }
 
+// The dispatcher hands workgroup i to XCD i % 8.  With H workgroups per
+// sequence (KV heads x chunks) in plain order, XCD x would read head tiles
+// x, x+8, x+16, ... of every block: tiles a fixed stride apart.  This
+// renumbering gives XCD x the H/8 consecutive head tiles x*H/8 .. of each
+// sequence instead, so every XCD reads one contiguous stretch of each block.
+// A bijection on [0, gridDim.x) when H % 8 == 0 (the grid is then a multiple
+// of 8); otherwise the identity.
+__device__ __forceinline__ int xcd_contiguous_heads(int i, int H) {
+  if (H % 8 != 0) return i;
+  const int per = H / 8, x = i % 8, j = i / 8;
+  return (j / per) * H + x * per + j % per;
+}
+
 // The (KV head, head chunk, sequence, partition) a workgroup works on.
 // Split-K launches follow the plan written by k_plan: workgroup index
 // (unit, KV head, chunk), units longest first, so the dispatcher schedules
 // long pieces before short ones (longest-first list scheduling); workgroups
-// past the plan's unit count exit.  A single pass has one unit per sequence.
+// past the plan's unit count exit.  A single pass has one unit per sequence,
+// with the workgroups of each sequence spread over the XCDs in contiguous
+// head ranges (above).
 struct Unit {
   int ch, g, s, p;
 };
 __device__ __forceinline__ bool resolve_unit(const KArgs& a, Unit& u) {
-  int wg = blockIdx.x;
+  int wg = a.units != nullptr ? (int)blockIdx.x
+                              : xcd_contiguous_heads(blockIdx.x, a.chunks * a.num_kv_heads);
   u.ch = wg % a.chunks;  wg /= a.chunks;
   u.g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
   if (a.units != nullptr) {
