@@ -71,3 +71,12 @@ def test_cpu_baseline_record_on_the_tiny_workload():
     assert str(kv_token_count(case)) in rec["sample"]
     one = rec["one_worker"]
     assert one["cores"] == 1 and one["value"] > 0
+
+
+@pytest.mark.gpu
+def test_read_sweep_mode_prints_one_json_line():
+    r = _bench("--read-sweep")
+    assert r.returncode == 0, r.stderr[-2000:]
+    rec = json.loads([l for l in r.stdout.splitlines() if l.strip()][-1])
+    assert [x["tile_bytes"] for x in rec["rows"]] == [4096, 8192, 16384, 32768, 65536]
+    assert all(x["in_order_GBps"] > 0 and x["random_GBps"] > 0 for x in rec["rows"])
