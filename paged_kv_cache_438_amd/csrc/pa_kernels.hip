@@ -239,6 +239,7 @@ struct KArgs {
   int chunks;           // group / GW
   int part_tokens;      // P
   int max_parts;
+  int xcd_heads;        // consecutive workgroups of a unit per XCD (xcd_group)
   float scale_log2;     // scale * log2(e)
 };
 
@@ -301,6 +302,23 @@ __device__ __forceinline__ SeqLayout seq_layout(const KArgs& a, int s) {
   return layout_of(a, a.lens[s], gi, lp, cnt);
 }
 
+// The dispatcher hands workgroup i to XCD i % 8.  In plain order, with H
+// workgroups (KV heads x chunks) per unit, XCD x would read head tiles x,
+// x+8, x+16, ... of every block it touches: tiles a fixed stride apart.
+// xcd_group renumbers the workgroups so that each XCD takes c consecutive
+// head tiles of a unit at a time: the units' groups of c heads are dealt to
+// the XCDs in turn, in unit order, so every XCD reads contiguous stretches of
+// c tiles and the longest-first order of a split-K plan is kept up to groups
+// of c units.  The host picks c (1: plain order).  A bijection on
+// [0, gridDim.x) when c divides H and 8c divides the grid.
+__device__ __forceinline__ int xcd_group(int i, int H, int c) {
+  if (c <= 1) return i;
+  const int x = i % 8, j = i / 8;
+  const int grp = (j / c) * 8 + x;            // global index of the c-head group
+  const int per_unit = H / c;
+  return (grp / per_unit) * H + (grp % per_unit) * c + j % c;
+}
+
 // One query column of a matrix-core workgroup: whose query it is, which
 // partition slot of that sequence it fills, and whether it writes the output
 // directly (the sequence has a single partition).
@@ -321,7 +339,7 @@ struct KUnit {
   bool bad, tail;
 };
 __device__ __forceinline__ bool resolve_kunit(const KArgs& a, KUnit& u, SeqLayout& lay) {
-  int wg = blockIdx.x;
+  int wg = xcd_group(blockIdx.x, a.chunks * a.num_kv_heads, a.xcd_heads);
   u.ch = wg % a.chunks;  wg /= a.chunks;
   u.g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
   int x = wg, y = 0;
@@ -383,32 +401,18 @@ __device__ __forceinline__ Col column_of(const KArgs& a, const KUnit& u, const S
   return c;
 }
 
-// The dispatcher hands workgroup i to XCD i % 8.  With H workgroups per
-// sequence (KV heads x chunks) in plain order, XCD x would read head tiles
-// x, x+8, x+16, ... of every block: tiles a fixed stride apart.  This
-// renumbering gives XCD x the H/8 consecutive head tiles x*H/8 .. of each
-// sequence instead, so every XCD reads one contiguous stretch of each block.
-// A bijection on [0, gridDim.x) when H % 8 == 0 (the grid is then a multiple
-// of 8); otherwise the identity.
-__device__ __forceinline__ int xcd_contiguous_heads(int i, int H) {
-  if (H % 8 != 0) return i;
-  const int per = H / 8, x = i % 8, j = i / 8;
-  return (j / per) * H + x * per + j % per;
-}
-
 // The (KV head, head chunk, sequence, partition) a workgroup works on.
 // Split-K launches follow the plan written by k_plan: workgroup index
 // (unit, KV head, chunk), units longest first, so the dispatcher schedules
 // long pieces before short ones (longest-first list scheduling); workgroups
-// past the plan's unit count exit.  A single pass has one unit per sequence,
-// with the workgroups of each sequence spread over the XCDs in contiguous
-// head ranges (above).
+// past the plan's unit count exit.  A single pass has one unit per sequence.
+// Either way the workgroups are dealt to the XCDs in groups of consecutive
+// heads (above).
 struct Unit {
   int ch, g, s, p;
 };
 __device__ __forceinline__ bool resolve_unit(const KArgs& a, Unit& u) {
-  int wg = a.units != nullptr ? (int)blockIdx.x
-                              : xcd_contiguous_heads(blockIdx.x, a.chunks * a.num_kv_heads);
+  int wg = xcd_group(blockIdx.x, a.chunks * a.num_kv_heads, a.xcd_heads);
   u.ch = wg % a.chunks;  wg /= a.chunks;
   u.g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
   if (a.units != nullptr) {
@@ -1746,6 +1750,12 @@ hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t ld
 #define PA_SPLIT_WAVES 8
 #endif
 
+// Bytes of consecutive head tiles of one block that an XCD reads as a group
+// (xcd_group).
+#ifndef PA_XCD_GROUP_BYTES
+#define PA_XCD_GROUP_BYTES 8192
+#endif
+
 #ifndef PA_REDUCE_MAX_WGS
 #define PA_REDUCE_MAX_WGS 1024
 #endif
@@ -1875,6 +1885,17 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
                               : (long long)(p.num_seqs + (shared ? p.num_groups : 0)) * p.max_partitions;
   const long long grid = (long long)ka.chunks * p.num_kv_heads * units;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // Heads per XCD group: the largest power of two c with c tiles of one
+  // (block, KV head) within PA_XCD_GROUP_BYTES, c dividing the workgroups of
+  // a unit and 8c dividing the grid (so the renumbering is a bijection).
+  {
+    const long long tile = (long long)p.head_dim * (p.dtype == kF32 ? 4 : 2) * p.block_size;
+    const int H = ka.chunks * p.num_kv_heads;
+    int c = 1;
+    while (2LL * c * tile <= PA_XCD_GROUP_BYTES && H % (2 * c) == 0 && grid % (16LL * c) == 0)
+      c *= 2;
+    ka.xcd_heads = c;
+  }
 
   hipError_t e;
   if (ws != nullptr) {
