@@ -1254,12 +1254,19 @@ struct PArgs {
   int max_group_size;
 };
 
-// Exclusive prefix sum of n ints (src -> dst, dst[n] = total) by one
-// workgroup of 1024 threads, 1024 entries at a time.
+// Threads of the plan's single workgroup.
+#ifndef PA_PLAN_THREADS
+#define PA_PLAN_THREADS 256
+#endif
+constexpr int kPlanThreads = PA_PLAN_THREADS;
+static_assert(kPlanThreads % 64 == 0 && kPlanThreads >= 256, "plan workgroup");
+
+// Exclusive prefix sum of n ints (src -> dst, dst[n] = total) by the plan's
+// workgroup, kPlanThreads entries at a time.
 __device__ __forceinline__ void block_exclusive_scan(const int* src, int* dst, int n, int* s_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int carry = 0;
-  for (int base = 0; base < n; base += 1024) {
+  for (int base = 0; base < n; base += kPlanThreads) {
     const int v = base + tid < n ? src[base + tid] : 0;
     int incl = v;
 #pragma unroll
@@ -1273,7 +1280,7 @@ __device__ __forceinline__ void block_exclusive_scan(const int* src, int* dst, i
     for (int w = 0; w < wv; ++w) before += s_tot[w];
     if (base + tid < n) dst[base + tid] = before + incl - v;
     int chunk = 0;
-    for (int w = 0; w < 16; ++w) chunk += s_tot[w];
+    for (int w = 0; w < kPlanThreads / 64; ++w) chunk += s_tot[w];
     __syncthreads();
     carry += chunk;
   }
@@ -1296,9 +1303,9 @@ constexpr int kPlanGroups = 1024;
 // in ascending sequence order) and the reduce's order are fixed.
 // Lengths, groups and group tables are staged in LDS, so the phases below
 // touch global memory only to load them and to write the plan.
-__global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   __shared__ int hist[257];           // bucket counts, then starts (+ total)
-  __shared__ int s_tot[16];
+  __shared__ int s_tot[kPlanThreads / 64];
   __shared__ int s_split;             // sequences with more than one partition
   __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_arr[kPlanSeqs];
   __shared__ int s_gfill[kPlanGroups], s_gstart[kPlanGroups + 1], s_glp[kPlanGroups];
@@ -1314,12 +1321,12 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
   int* glp = lds_groups ? s_glp : pa.group_lp;
   if (tid < 256) hist[tid] = 0;
   if (tid == 0) s_split = 0;
-  for (int i = tid; i < NG; i += 1024) gfill[i] = 0;
-  for (int s = tid; s < min(B, kPlanSeqs); s += 1024) {
+  for (int i = tid; i < NG; i += kPlanThreads) gfill[i] = 0;
+  for (int s = tid; s < min(B, kPlanSeqs); s += kPlanThreads) {
     s_len[s] = a.lens[s];
     s_grp[s] = shared ? a.seq_group[s] : -1;
   }
-  for (int i = tid; i < NG; i += 1024) glp[i] = a.group_prefix[i];   // checked below
+  for (int i = tid; i < NG; i += kPlanThreads) glp[i] = a.group_prefix[i];   // checked below
   __syncthreads();
   auto len_of = [&](int s) { return s < kPlanSeqs ? s_len[s] : a.lens[s]; };
   auto grp_of = [&](int s) { return !shared ? -1 : (s < kPlanSeqs ? s_grp[s] : a.seq_group[s]); };
@@ -1334,14 +1341,14 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
   };
   if (shared) {
     // Members of each group, grouped by a counting sort.
-    for (int s = tid; s < B; s += 1024) {
+    for (int s = tid; s < B; s += kPlanThreads) {
       const int gi = grp_of(s);
       if (gi >= 0 && gi < NG) atomicAdd(&gfill[gi], 1);
     }
     __syncthreads();
     block_exclusive_scan(gfill, gstart, NG, s_tot);
     __syncthreads();
-    for (int i = tid; i < NG; i += 1024) {
+    for (int i = tid; i < NG; i += kPlanThreads) {
       // A prompt that is not whole blocks, longer than a table can hold, cut
       // into more partitions than a sequence may have, or shared by more
       // members than the launch's column chunks cover is out of contract:
@@ -1360,12 +1367,12 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
     // arrival order, then each placed at its rank among its group's members.
     const int nmem = gstart[NG];
     int* arrival = nmem <= kPlanSeqs ? s_arr : reinterpret_cast<int*>(pa.units);
-    for (int s = tid; s < B; s += 1024) {
+    for (int s = tid; s < B; s += kPlanThreads) {
       const int gi = grp_of(s);
       if (gi >= 0 && gi < NG) arrival[gstart[gi] + atomicAdd(&gfill[gi], 1)] = s;
     }
     __syncthreads();
-    for (int x = tid; x < nmem; x += 1024) {
+    for (int x = tid; x < nmem; x += kPlanThreads) {
       const int s = arrival[x];
       const int gi = grp_of(s);
       const int lo = gstart[gi], hi = gstart[gi + 1];
@@ -1373,11 +1380,11 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
       for (int y = lo; y < hi; ++y) rank += arrival[y] < s;
       pa.members[lo + rank] = s;
     }
-    for (int i = tid; i < NG; i += 1024) gfill[i] = 0;
+    for (int i = tid; i < NG; i += kPlanThreads) gfill[i] = 0;
     __syncthreads();
     // gfill[gi] <- absorbed own tokens of the group per column chunk (at
     // most about P by the absorption bound).
-    for (int s = tid; s < B; s += 1024) {
+    for (int s = tid; s < B; s += kPlanThreads) {
       const SeqLayout ml = layout(s);
       if (ml.bad || !ml.absorbed) continue;
       const int gi = grp_of(s);
@@ -1412,13 +1419,13 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
         for (int i = 0; i < n; ++i) pa.units[at + i] = make_int2(x, y0 + i);
       }
     };
-    for (int gi = tid; gi < NG; gi += 1024) {
+    for (int gi = tid; gi < NG; gi += kPlanThreads) {
       const int np = prompt_parts(gi);
       put(P, -(gi + 1), 0, np - 1);
       // the last partition: the rest of the prompt plus absorbed own tokens
       if (np > 0) put(glp[gi] - (np - 1) * P + gfill[gi], -(gi + 1), np - 1, 1);
     }
-    for (int s = tid; s < B; s += 1024) {
+    for (int s = tid; s < B; s += kPlanThreads) {
       const SeqLayout lay = layout(s);
       const int own = lay.nparts - lay.np_pre;
       if (pass == 0 && lay.nparts > 1) pa.split[atomicAdd(&s_split, 1)] = s;
@@ -1442,8 +1449,8 @@ __global__ __launch_bounds__(1024) void k_plan(const PArgs pa) {
   }
   // The group tables the partition and reduce launches read.
   if (shared && lds_groups) {
-    for (int i = tid; i <= NG; i += 1024) pa.group_start[i] = gstart[i];
-    for (int i = tid; i < NG; i += 1024) pa.group_lp[i] = glp[i];
+    for (int i = tid; i <= NG; i += kPlanThreads) pa.group_start[i] = gstart[i];
+    for (int i = tid; i < NG; i += kPlanThreads) pa.group_lp[i] = glp[i];
   }
 }
 
@@ -1910,7 +1917,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     pa_.members = shared ? reinterpret_cast<int*>(ws + wl.members) : nullptr;
     pa_.group_lp = shared ? reinterpret_cast<int*>(ws + wl.group_lp) : nullptr;
     pa_.max_group_size = p.max_group_size;
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, stream, pa_);
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, pa_);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
