@@ -151,6 +151,40 @@ def test_grouped_heads_both_paths(spec):
                     assert np.all(got[s_] == 0.0)
 
 
+# ------------------------------------------------------------------ XCD head groups
+_L16 = (1, 15, 16, 17, 31, 33, 64, 100, 129, 200, 255, 256, 257, 300, 0, 77)
+XCD_GROUPED = [
+    # Shapes whose launches deal the workgroups of each unit to the XCDs in
+    # groups of c consecutive heads (c tiles within 8 KiB, c dividing the
+    # unit's workgroups, 8c dividing the grid): every output must still come
+    # from exactly one workgroup.
+    # (name, lens, Hq, Hkv, d, bs, dtype, partition)
+    ("mha_f16_d128_bs16_c2", _L16, 8, 8, 128, 16, "f16", 64),
+    ("mha_f16_d64_bs16_c4", _L16, 8, 8, 64, 16, "f16", 64),
+    ("mha_bf16_d128_bs1_c8", _L16, 8, 8, 128, 1, "bf16", 64),
+    ("mha_f32_d64_bs16_c2", _L16, 8, 8, 64, 16, "f32", 64),
+    ("gqa_f16_d128_bs16_c2", _L16, 32, 8, 128, 16, "f16", 64),
+    ("gqa_bf16_d64_bs8_c4", _L16 + tuple(L + 3 for L in _L16), 16, 4, 64, 8, "bf16", 64),
+]
+
+
+@pytest.mark.parametrize("spec", XCD_GROUPED, ids=lambda s: s[0])
+def test_xcd_head_groups_cover_every_unit(spec):
+    w = edge_workload(*spec)
+    c = make_case(w)
+    ref = _oracle(c)
+    d = DevCase(c)
+    for valu in ((False, True) if w.num_heads > w.num_kv_heads else (False,)):
+        for entry, P in (("single", None), ("splitk", w.partition_size), ("splitk", 16)):
+            note(f"xcd groups: {w.name} valu_only={valu} entry={entry} P={P}")
+            got = host_f64(d.decode(entry, P, valu_only=valu))
+            torch.cuda.synchronize()
+            _check_close(got, ref, w.dtype, f"{w.name}/valu={valu}/{entry}/{P}")
+            for s_, L in enumerate(w.lengths):
+                if L == 0:
+                    assert np.all(got[s_] == 0.0)
+
+
 # ------------------------------------------------------------------ bit-exact indexing
 def _needle_case(w, seed):
     """Every query is 32*e_0; key component 0 is 0 everywhere except one
