@@ -227,6 +227,14 @@ def read_ceiling(pa, torch, seed: int = 5) -> dict:
         torch.cuda.synchronize()
         res[name + "_GBps"] = round(total / (a.elapsed_time(b) / 10 * 1e-3) / 1e9, 1)
     del buf
+    # The runtime's own figures: bus width and peak memory clock.  MI355X
+    # reports 8192 bits at 2.0 GHz; its HBM3E pins run at about 8 Gb/s, i.e.
+    # 4 transfers per reported clock, which implies 8.19 TB/s (the roofline
+    # uses the published 8 TB/s).
+    bw_bits, clk_khz = pa.pa_device_memory(torch.cuda.current_device())
+    res["device_reported"] = {"bus_width_bits": bw_bits, "mem_clock_khz": clk_khz,
+                              "transfers_per_clock": 4,
+                              "implied_peak_GBps": round(4 * clk_khz * 1e3 * bw_bits / 8 / 1e9, 1)}
     return res
 
 

@@ -293,6 +293,15 @@ int pa_read_probe(const void* buf, size_t tile_bytes, const int32_t* tile_order,
                   uint32_t* sink, void* stream);
 
 /*
+ * pa_device_memory -- a measurement aid: the memory bus width in bits and the
+ * peak memory clock in kHz that the HIP runtime reports for `device`, written
+ * to *bus_width_bits and *mem_clock_khz (HOST ints).  Returns PA_ERR_NULL for a
+ * NULL output pointer, PA_ERR_HIP (with the runtime's message in
+ * pa_last_error) if the device cannot be queried.  Launches nothing.
+ */
+int pa_device_memory(int device, int* bus_width_bits, int* mem_clock_khz);
+
+/*
  * pa_check_inputs_host -- validate HOST copies of the device data against the
  * contract above: 0 <= L <= max_blocks_per_seq * block_size, every table entry
  * in use in [0, num_blocks), and, if check_write_targets is nonzero, that no

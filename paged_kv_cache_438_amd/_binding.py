@@ -33,6 +33,7 @@ _SIGNATURES = {
                          [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
                           _c_void_p]),
     "pa_read_probe": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p, _c_void_p]),
+    "pa_device_memory": (_c_int, [_c_int, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
                              [ctypes.POINTER(_c_int)]),
     "pa_decode_shared_prefix_workspace_bytes": (_c_size_t, [_c_int] * 6),
@@ -333,6 +334,14 @@ def pa_read_probe(buf: torch.Tensor, tile_bytes: int, tile_order: torch.Tensor,
     st = load().pa_read_probe(buf.data_ptr(), tile_bytes, tile_order.data_ptr(),
                               tile_order.numel(), sink.data_ptr(), _stream(buf.device, stream))
     _check(st, "pa_read_probe")
+
+
+def pa_device_memory(device: int = 0) -> Tuple[int, int]:
+    """(memory bus width in bits, peak memory clock in kHz) as the HIP runtime
+    reports them for ``device``; a measurement aid (see include/pa.h)."""
+    bw, clk = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().pa_device_memory(device, ctypes.byref(bw), ctypes.byref(clk)), "pa_device_memory")
+    return bw.value, clk.value
 
 
 def pa_check_inputs_host(block_tables, context_lens, block_size: int, num_blocks: int,

@@ -387,6 +387,15 @@ int pa_read_probe(const void* buf, size_t tile_bytes, const int32_t* tile_order,
                                              static_cast<hipStream_t>(stream)));
 }
 
+int pa_device_memory(int device, int* bus_width_bits, int* mem_clock_khz) {
+  if (!bus_width_bits || !mem_clock_khz) return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
+  hipError_t e = hipDeviceGetAttribute(bus_width_bits, hipDeviceAttributeMemoryBusWidth, device);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(mem_clock_khz, hipDeviceAttributeMemoryClockRate, device);
+  if (e != hipSuccess) return pa_fail(PA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  return pa_ok();
+}
+
 int pa_check_inputs_host(const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                          int block_size, int max_blocks_per_seq, int num_blocks,
                          int check_write_targets, int* bad_seq) {

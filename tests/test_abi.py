@@ -81,6 +81,7 @@ def test_cache_write_rejects(lib):
 def test_read_probe_rejects(lib):
     assert lib.pa_read_probe(P, 1000, P, 4, P, None) == 2          # not a multiple of 4096
     assert lib.pa_read_probe(P, 4096, P, -1, P, None) == 2
+    assert lib.pa_device_memory(0, None, None) == 1                # NULL outputs, no device query
     assert lib.pa_read_probe(0, 4096, P, 4, P, None) == 1
     assert lib.pa_read_probe(P + 8, 4096, P, 4, P, None) == 2      # misaligned buffer
     assert lib.pa_read_probe(0, 4096, 0, 0, 0, None) == 0          # nothing to read
