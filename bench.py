@@ -427,7 +427,8 @@ def main() -> int:
         evs[i][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    dec_all = [a.elapsed_time(b) for a, b in evs]
+    dec_ms = float(np.mean(dec_all))
 
     e = w.elem_bytes
     # With prompt groups the blocks a group shares are counted once (unique
@@ -486,6 +487,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kernel,
                      "avg_launch_us": round(dec_ms * 1e3, 3),
+                     "median_launch_us": round(float(np.median(dec_all)) * 1e3, 3),
                      "algorithmic_bytes_per_launch": dec_bytes,
                      "logical_bytes_per_launch": logical_bytes},
         "cpu_baseline": cpu,
