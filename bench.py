@@ -27,6 +27,8 @@ sys.path.insert(0, str(ROOT))
 from synthetic import WORKLOADS, algorithmic_bytes, kv_token_count, make_case  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+# Max-abs error bounds against the fp64 oracle, fp32 accumulation.
+TOLERANCE = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and KV tokens/sec"
 # Entry point and partition size per workload.  The long-context workload is
 # specified with 512-token partitions; the grouped-query batch uses 8192-token
@@ -64,16 +66,40 @@ def _oracle_one(s):
     return s, o
 
 
-def cpu_baseline(case, min_seconds: float) -> dict:
-    """Time the fp64 oracle over whole passes of the workload (all sequences,
-    all heads) with a fork pool, until at least ``min_seconds`` have passed."""
-    global _CASE
-    _CASE = case
+def _assemble(case, res) -> np.ndarray:
+    """Oracle rows from a pool pass, as one fp64 [B][Hq][d] array."""
+    w = case.workload
+    ref = np.full((w.num_seqs, w.num_heads, w.head_dim), np.nan, dtype=np.float64)
+    for s, o in res:
+        ref[s] = o[0]
+    return ref
+
+
+def _workers() -> int:
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
-    workers = max(1, min(avail, 16))
+    return max(1, min(avail, 16))
+
+
+def oracle_reference(case) -> np.ndarray:
+    """One fp64 oracle pass over every (sequence, head) row, for the check
+    of the timed output when the CPU baseline is not measured."""
+    global _CASE
+    _CASE = case
+    order = list(np.argsort(-case.context_lens.astype(np.int64)))
+    with mp.get_context("fork").Pool(_workers(), initializer=_worker_init) as pool:
+        return _assemble(case, pool.map(_oracle_one, order, chunksize=1))
+
+
+def cpu_baseline(case, min_seconds: float):
+    """Time the fp64 oracle over whole passes of the workload (all sequences,
+    all heads) with a fork pool, until at least ``min_seconds`` have passed.
+    Returns the last pass's output (every row) and the baseline record."""
+    global _CASE
+    _CASE = case
+    workers = _workers()
     B = case.workload.num_seqs
     tokens = kv_token_count(case)
     order = list(np.argsort(-case.context_lens.astype(np.int64)))   # longest first
@@ -88,6 +114,7 @@ def cpu_baseline(case, min_seconds: float) -> dict:
             if el >= min_seconds or passes >= 1000:
                 break
     assert len(res) == B
+    ref = _assemble(case, res)
     # The same passes in this process alone, BLAS held to one thread: the
     # single-core rate.
     try:
@@ -114,14 +141,14 @@ def cpu_baseline(case, min_seconds: float) -> dict:
                 break
     except OSError:
         pass
-    return {"value": passes * tokens / el, "unit": "KV tokens/s", "cores": workers,
-            "kind": "oracle",
-            "sample": f"{passes} full pass(es) over all {B} sequences x "
-                      f"{case.workload.num_heads} heads ({tokens} KV tokens per pass), "
-                      f"fp64 NumPy, fork pool of {workers} workers, {el:.1f} s wall",
-            "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
-            "one_worker": {"value": passes1 * tokens / el1, "unit": "KV tokens/s", "cores": 1,
-                           "sample": f"{passes1} full pass(es) in one process, {el1:.1f} s wall"}}
+    return ref, {
+        "value": passes * tokens / el, "unit": "KV tokens/s", "cores": workers, "kind": "oracle",
+        "sample": f"{passes} full pass(es) over all {B} sequences x "
+                  f"{case.workload.num_heads} heads ({tokens} KV tokens per pass), "
+                  f"fp64 NumPy, fork pool of {workers} workers, {el:.1f} s wall",
+        "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
+        "one_worker": {"value": passes1 * tokens / el1, "unit": "KV tokens/s", "cores": 1,
+                       "sample": f"{passes1} full pass(es) in one process, {el1:.1f} s wall"}}
 
 
 # ----------------------------------------------------------------- traffic records
@@ -283,6 +310,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true",
+                    help="do not compare the timed output with the oracle (profiler runs)")
     ap.add_argument("--block-size", type=int, default=None,
                     help="override the workload's block size (page-size sweep)")
     ap.add_argument("--contiguous", action="store_true",
@@ -349,10 +378,13 @@ def main() -> int:
     log(f"bench: generated {w.name} seed={case.seed} in {time.perf_counter() - t:.1f} s; "
         f"sum L = {kv_token_count(case)}, pool blocks = {case.num_blocks}")
 
-    cpu = None
+    # The oracle runs in fork pools before any GPU call.
+    cpu, ref = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, args.cpu_seconds)      # before any GPU call (fork)
+        ref, cpu = cpu_baseline(case, args.cpu_seconds)
         log(f"bench: cpu baseline {cpu['value']:.4g} KV tokens/s on {cpu['cores']} workers")
+    elif not args.no_check:
+        ref = oracle_reference(case)
 
     import torch
     import paged_kv_cache_438_amd as pa
@@ -442,6 +474,15 @@ def main() -> int:
     tokens = kv_token_count(case)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
+    # The output of the last timed step against the fp64 oracle, every
+    # (sequence, head) row, within the storage dtype's max-abs bound.
+    tol = TOLERANCE[dt]
+    max_err = None
+    if ref is not None:
+        got = out.float().cpu().numpy().astype(np.float64)
+        max_err = float(np.max(np.abs(got - ref))) if np.all(np.isfinite(got)) else float("inf")
+        log(f"bench: timed output vs oracle: max|err| = {max_err:.3e} (bound {tol:.0e})")
+
     ceiling = read_ceiling(pa, torch) if not args.no_read_ceiling else None
     if ceiling:
         ceiling["decode_frac_of_random_tiles"] = round(achieved / ceiling["random_tiles_GBps"], 4)
@@ -481,6 +522,12 @@ def main() -> int:
                    "valu_only": bool(args.valu_only),
                    "global_batch": w.num_seqs, "kv_tokens": tokens,
                    "step": "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
+        "max_abs_err": max_err,
+        "tolerance": tol,
+        "check": ("output of the last timed step vs the fp64 oracle, all "
+                  f"{w.num_seqs * w.num_heads} (sequence, head) rows") if ref is not None
+                 else "skipped (--no-check)",
+        "pool_utilization": round(case.unique_blocks / case.num_blocks, 4),
         "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -494,6 +541,9 @@ def main() -> int:
         "read_ceiling": ceiling,
     }
     print(json.dumps(res), flush=True)
+    if max_err is not None and not max_err <= tol:
+        log(f"bench: FAILED: timed output differs from the oracle by {max_err} > {tol}")
+        return 1
     return 0
 
 

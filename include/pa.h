@@ -26,10 +26,11 @@
  *
  * Ownership and execution: every pointer argument is a DEVICE pointer owned by
  * the caller (except pa_check_inputs_host, which takes HOST pointers).  The
- * library allocates nothing and keeps no pointer after a call returns.  Every
- * call only enqueues work on `stream` (a hipStream_t; NULL = the null stream)
- * and returns without synchronising.  Calls are thread-safe; the only global
- * state is the calling thread's last-error string.
+ * library allocates nothing and keeps no caller pointer after a call returns.
+ * Every call only enqueues work on `stream` (a hipStream_t passed as void*;
+ * NULL = the null stream) and returns without synchronising.  Calls are
+ * thread-safe; the only global state is the calling thread's last-error
+ * string.
  *
  * Errors: the host-side scalar checks below run before anything is enqueued; a
  * failing call returns a nonzero pa_status, enqueues nothing and records a

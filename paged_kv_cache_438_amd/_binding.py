@@ -186,13 +186,13 @@ def _decode_args(q, k_pool, v_pool, block_tables, context_lens, scale, out):
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
     if scale is None:
-        scale = 1.0 / float(d) ** 0.5
+        raise TypeError("scale is required (usually 1/sqrt(head_dim), as an fp32 value)")
     return out, (B, Hq, Hkv, d, bs, MB, NB), float(scale)
 
 
 def pa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
               block_tables: torch.Tensor, context_lens: torch.Tensor,
-              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+              scale: float, out: Optional[torch.Tensor] = None,
               shared_kv: bool = False, valu_only: bool = False, stream=None) -> torch.Tensor:
     """Single-pass paged decode attention; returns ``out`` [num_seqs][num_heads][head_dim].
     ``shared_kv``: some blocks appear in several sequences' tables (keeps K/V
@@ -218,7 +218,7 @@ def pa_decode_splitk_workspace_bytes(num_seqs: int, num_heads: int, head_dim: in
 def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                      block_tables: torch.Tensor, context_lens: torch.Tensor,
                      partition_size: int, max_context_len: int,
-                     scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     scale: float, out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, shared_kv: bool = False,
                      valu_only: bool = False, stream=None) -> torch.Tensor:
     """Split-K paged decode attention (partition pass + reduce pass)."""
@@ -250,7 +250,7 @@ def pa_decode_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
                             block_tables: torch.Tensor, context_lens: torch.Tensor,
                             seq_group: torch.Tensor, group_prefix_len: torch.Tensor,
                             max_group_size: int, partition_size: int, max_context_len: int,
-                            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                            scale: float, out: Optional[torch.Tensor] = None,
                             workspace: Optional[torch.Tensor] = None, shared_kv: bool = False,
                             stream=None) -> torch.Tensor:
     """Decode for groups of sequences sharing a prompt's blocks; see

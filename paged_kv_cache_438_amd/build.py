@@ -33,19 +33,39 @@ def compile_flags() -> list:
 
 
 def build(verbose: bool = False) -> pathlib.Path:
-    """Compile every source into libpa.so (always recompiles)."""
+    """Compile every source into libpa.so (always recompiles).  The sources
+    are compiled to objects in parallel, then linked."""
+    objdir = ROOT / "_build"
+    objdir.mkdir(exist_ok=True)
+    flags = [f for f in compile_flags() if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = objdir / (src.name + ".o")
+        cmd = [hipcc()] + flags + ["-c", str(src), "-o", str(obj)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((cmd, obj, subprocess.Popen(cmd, cwd=str(PKG), stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT, text=True)))
+    failed = False
+    for cmd, obj, proc in jobs:
+        out, _ = proc.communicate()
+        noise = [ln for ln in out.splitlines() if ln.strip() and "packed-fp32-ops" not in ln]
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed = True
+        elif verbose and noise:
+            print("\n".join(noise), flush=True)
+    if failed:
+        raise RuntimeError("hipcc failed")
     tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc()] + compile_flags() + [str(s) for s in SOURCES] + ["-o", str(tmp)]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-fPIC", "-shared"] + \
+        [str(o) for _, o, _ in jobs] + ["-o", str(tmp)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, cwd=str(PKG), capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    noise = [ln for ln in (res.stdout + res.stderr).splitlines()
-             if ln.strip() and "packed-fp32-ops" not in ln]
-    if verbose and noise:
-        print("\n".join(noise), flush=True)
+        raise RuntimeError(f"hipcc link failed with status {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -267,12 +267,16 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
   return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
-int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v_pool,
-                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
-                     int num_heads, int num_kv_heads, int head_dim, int block_size,
-                     int max_blocks_per_seq, int num_blocks, float scale, int dtype,
-                     int partition_size, int max_context_len, void* workspace,
-                     size_t workspace_bytes, int flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch of the split-K entry.
+int splitk_checks(void* out, const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                  int num_heads, int num_kv_heads, int head_dim, int block_size,
+                  int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                  int partition_size, int max_context_len, int flags) {
   int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                         dtype, flags);
@@ -284,13 +288,15 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
     return pa_fail(PA_ERR_INVALID_ARG,
                 "max_context_len %d outside [0, max_blocks_per_seq*block_size = %lld]",
                 max_context_len, (long long)max_blocks_per_seq * block_size);
-  if (num_seqs == 0) return pa_ok();
-  const size_t need = pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim,
-                                                       max_context_len, partition_size);
-  if (!workspace || workspace_bytes < need)
-    return pa_fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
-                workspace_bytes, workspace ? "" : ", NULL");
-  if (!aligned16(workspace)) return pa_fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return PA_OK;
+}
+
+int splitk_launch(void* out, const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                  int num_heads, int num_kv_heads, int head_dim, int block_size,
+                  int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                  int partition_size, int max_context_len, void* workspace, int flags,
+                  void* stream) {
   pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                                    num_heads, num_kv_heads, head_dim, block_size,
                                    max_blocks_per_seq, num_blocks, scale, dtype, flags);
@@ -299,6 +305,32 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
   p.max_partitions = parts > 0 ? parts : 1;
   p.workspace = static_cast<float*>(workspace);
   return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                     int num_heads, int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                     int partition_size, int max_context_len, void* workspace,
+                     size_t workspace_bytes, int flags, void* stream) {
+  int st = splitk_checks(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                         scale, dtype, partition_size, max_context_len, flags);
+  if (st) return st;
+  if (num_seqs == 0) return pa_ok();
+  const size_t need = pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                       max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need)
+    return pa_fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return pa_fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return splitk_launch(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       dtype, partition_size, max_context_len, workspace, flags, stream);
 }
 
 int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,
@@ -344,6 +376,9 @@ int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_
       void* host_v = to_host ? dst_v : const_cast<void*>(src_v);
       void* mk = nullptr;
       void* mv = nullptr;
+      // An error left by an earlier call is the caller's: clear only the one
+      // a failed lookup below leaves.
+      const bool clean_before = hipPeekAtLastError() == hipSuccess;
       if (hipHostGetDevicePointer(&mk, host_k, 0) == hipSuccess &&
           hipHostGetDevicePointer(&mv, host_v, 0) == hipSuccess && mk && mv) {
         const hipError_t e =
@@ -352,7 +387,7 @@ int pa_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_
         if (e != hipSuccess) return pa_fail(PA_ERR_HIP, "swap launch failed: %s", hipGetErrorString(e));
         return pa_ok();
       }
-      (void)hipGetLastError();   // not mapped: clear the error, copy below
+      if (clean_before) (void)hipGetLastError();   // not mapped: copy below
     }
   }
   // Runs of pairs whose sources and destinations are both consecutive go out

@@ -844,37 +844,50 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&w)[4], int a) {
 // vmcnt(n) for the slot's loads, lgkmcnt(0) before a slot is refilled.  The
 // compiler would otherwise wait for every outstanding direct-to-LDS load
 // before any LDS read, which serialises the two slots.
-__device__ __forceinline__ uint4 lds_read16(uint32_t addr) {
-  uint4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-  return v;
-}
+//
+// All operand reads of a step and the lgkmcnt(0) that waits for them are one
+// asm statement: the compiler takes an asm output as ready when the asm ends,
+// so with the wait inside it no use, copy or spill of an operand can be
+// placed before the data has arrived.  The outputs are early-clobber: a read
+// in flight must not land in a register that a later read of the same
+// statement still takes its address from.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <int N> struct LdsReads;
+template <> struct LdsReads<4> {   // head_dim 64: 2 K + 2 V operands
+  static __device__ __forceinline__ void run(u32x4_t (&o)[4], const uint32_t (&ad)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  }
+};
+template <> struct LdsReads<8> {   // head_dim 128: 4 K + 4 V operands
+  static __device__ __forceinline__ void run(u32x4_t (&o)[8], const uint32_t (&ad)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]),
+          "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]),
+          "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+  }
+};
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-// An empty asm that the compiler sees as rewriting the registers of operands
-// read from LDS by assembly.  The compiler takes an asm output as ready when
-// the asm ends; placed after the wait for those reads, this keeps every use,
-// copy or spill of the operands below the wait.
-template <int N>
-__device__ __forceinline__ void tie_operands(uint4 (&b)[N]);
-template <>
-__device__ __forceinline__ void tie_operands<4>(uint4 (&b)[4]) {
-  asm volatile(""
-               : "+v"(b[0].x), "+v"(b[0].y), "+v"(b[0].z), "+v"(b[0].w),
-                 "+v"(b[1].x), "+v"(b[1].y), "+v"(b[1].z), "+v"(b[1].w),
-                 "+v"(b[2].x), "+v"(b[2].y), "+v"(b[2].z), "+v"(b[2].w),
-                 "+v"(b[3].x), "+v"(b[3].y), "+v"(b[3].z), "+v"(b[3].w));
-}
-template <>
-__device__ __forceinline__ void tie_operands<2>(uint4 (&b)[2]) {
-  asm volatile(""
-               : "+v"(b[0].x), "+v"(b[0].y), "+v"(b[0].z), "+v"(b[0].w),
-                 "+v"(b[1].x), "+v"(b[1].y), "+v"(b[1].z), "+v"(b[1].w));
 }
 
 template <bool NT>
@@ -1078,18 +1091,25 @@ void k_decode_mfma(const KArgs a) {
     }
   };
   struct Ops { uint4 k[NI], v[NI]; };
-  // Operand reads from a slot: K of row n at chunk 4i + lg; V of row
-  // 4*lg + qa at chunk 4i + qb.
+  // Operand reads from a slot, waited for before they are returned: K of
+  // row n at chunk 4i + lg; V of row 4*lg + qa at chunk 4i + qb.
   auto read_ops = [&](int slot) {
-    Ops o;
     const uint32_t base = wave_lds_addr + slot * SLOT;
     const int vr = 4 * lg + qa;
+    uint32_t ad[2 * NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      o.k[i] = lds_read16(base + n * ROWB + swz_pos<D>(4 * i + lg, n) * 16);
+    for (int i = 0; i < NI; ++i) {
+      ad[i] = base + n * ROWB + swz_pos<D>(4 * i + lg, n) * 16;
+      ad[NI + i] = base + TILE + vr * ROWB + swz_pos<D>(4 * i + qb, vr) * 16;
+    }
+    u32x4_t r[2 * NI];
+    LdsReads<2 * NI>::run(r, ad);
+    Ops o;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      o.v[i] = lds_read16(base + TILE + vr * ROWB + swz_pos<D>(4 * i + qb, vr) * 16);
+    for (int i = 0; i < NI; ++i) {
+      o.k[i] = make_uint4(r[i].x, r[i].y, r[i].z, r[i].w);
+      o.v[i] = make_uint4(r[NI + i].x, r[NI + i].y, r[NI + i].z, r[NI + i].w);
+    }
     return o;
   };
   auto compute_step = [&](int k, const Ops& b) {
@@ -1172,11 +1192,8 @@ void k_decode_mfma(const KArgs a) {
     const int slot = k & 1;
     if (k + 1 < nk) wait_vmcnt<2 * NDMA>();   // the younger slot may stay in flight
     else wait_vmcnt<0>();
-    Ops ops = read_ops(slot);
-    wait_lgkmcnt0();                          // the slot is read: it may be refilled
+    const Ops ops = read_ops(slot);           // the slot is read: it may be refilled
     if (k + 2 < nk) issue(k + 2, slot);
-    tie_operands(ops.k);                      // uses of the operands stay below the wait
-    tie_operands(ops.v);
     compute_step(k, ops);
   }
 
@@ -1704,14 +1721,22 @@ int ilog2(int x) {
   return r;
 }
 
+// Launch a kernel that takes one argument struct and return the status of
+// this launch alone (not an error some earlier runtime call left behind).
+template <typename A>
+hipError_t launch1(void (*kernel)(A), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                   const A& arg) {
+  void* args[] = {const_cast<A*>(&arg)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, st);
+}
+
 template <int DT, int D, int W, int GW>
 hipError_t launch_decode_t(const KArgs& ka, bool big, bool nt, int grid, hipStream_t st) {
   const dim3 gd(grid), bd(W * 64);
-  if (big && nt) hipLaunchKernelGGL((k_decode<DT, D, W, GW, true, true>), gd, bd, 0, st, ka);
-  else if (big) hipLaunchKernelGGL((k_decode<DT, D, W, GW, true, false>), gd, bd, 0, st, ka);
-  else if (nt) hipLaunchKernelGGL((k_decode<DT, D, W, GW, false, true>), gd, bd, 0, st, ka);
-  else hipLaunchKernelGGL((k_decode<DT, D, W, GW, false, false>), gd, bd, 0, st, ka);
-  return hipGetLastError();
+  if (big && nt) return launch1(k_decode<DT, D, W, GW, true, true>, gd, bd, 0, st, ka);
+  if (big) return launch1(k_decode<DT, D, W, GW, true, false>, gd, bd, 0, st, ka);
+  if (nt) return launch1(k_decode<DT, D, W, GW, false, true>, gd, bd, 0, st, ka);
+  return launch1(k_decode<DT, D, W, GW, false, false>, gd, bd, 0, st, ka);
 }
 
 // Waves per workgroup: 16 only for one query head per wave and rows of at
@@ -1744,11 +1769,10 @@ hipError_t dispatch_d(const KArgs& ka, int d, int gw, int waves, bool big, bool 
 template <int DT, int D, int W>
 hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t lds, hipStream_t st) {
   const dim3 gd(grid), bd(W * 64);
-  if (big && nt) hipLaunchKernelGGL((k_decode_mfma<DT, D, W, true, true>), gd, bd, lds, st, ka);
-  else if (big) hipLaunchKernelGGL((k_decode_mfma<DT, D, W, true, false>), gd, bd, lds, st, ka);
-  else if (nt) hipLaunchKernelGGL((k_decode_mfma<DT, D, W, false, true>), gd, bd, lds, st, ka);
-  else hipLaunchKernelGGL((k_decode_mfma<DT, D, W, false, false>), gd, bd, lds, st, ka);
-  return hipGetLastError();
+  if (big && nt) return launch1(k_decode_mfma<DT, D, W, true, true>, gd, bd, lds, st, ka);
+  if (big) return launch1(k_decode_mfma<DT, D, W, true, false>, gd, bd, lds, st, ka);
+  if (nt) return launch1(k_decode_mfma<DT, D, W, false, true>, gd, bd, lds, st, ka);
+  return launch1(k_decode_mfma<DT, D, W, false, false>, gd, bd, lds, st, ka);
 }
 
 // Waves per workgroup of the vector kernel for partitions of 512 tokens or
@@ -1791,9 +1815,8 @@ hipError_t dispatch_mfma(const KArgs& ka, int d, bool big, bool nt, int grid, hi
 
 template <int DT>
 hipError_t launch_reduce_t(const KArgs& ka, int d, int grid, hipStream_t st) {
-  if (d == 64) hipLaunchKernelGGL((k_reduce<DT, 64>), dim3(grid), dim3(256), 0, st, ka);
-  else hipLaunchKernelGGL((k_reduce<DT, 128>), dim3(grid), dim3(256), 0, st, ka);
-  return hipGetLastError();
+  if (d == 64) return launch1(k_reduce<DT, 64>, dim3(grid), dim3(256), 0, st, ka);
+  return launch1(k_reduce<DT, 128>, dim3(grid), dim3(256), 0, st, ka);
 }
 
 }  // namespace
@@ -1917,8 +1940,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     pa_.members = shared ? reinterpret_cast<int*>(ws + wl.members) : nullptr;
     pa_.group_lp = shared ? reinterpret_cast<int*>(ws + wl.group_lp) : nullptr;
     pa_.max_group_size = p.max_group_size;
-    hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, pa_);
-    e = hipGetLastError();
+    e = launch1(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, pa_);
     if (e != hipSuccess) return e;
   }
   if (mfma) {
@@ -1955,8 +1977,7 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, 
   const size_t chunks = block_bytes / 16;
   const int pieces = (int)std::min<size_t>((chunks + 1023) / 1024, 64);   // 4 chunks per thread
   // (each thread of a piece then copies one round of four chunks of K and V)
-  hipLaunchKernelGGL(k_copy_blocks, dim3(pieces, num_pairs), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch1(k_copy_blocks, dim3(pieces, num_pairs), dim3(256), 0, stream, a);
 }
 
 hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
@@ -1974,8 +1995,7 @@ hipError_t launch_swap_blocks(void* dst_k, void* dst_v, const void* src_k, const
     a.num_pairs = std::min(kSwapPairs, num_pairs - first);
     for (int i = 0; i < a.num_pairs; ++i)
       a.pairs[i] = make_int2(pairs[2 * (first + i)], pairs[2 * (first + i) + 1]);
-    hipLaunchKernelGGL(k_swap_blocks, dim3(pieces, a.num_pairs), dim3(256), 0, stream, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch1(k_swap_blocks, dim3(pieces, a.num_pairs), dim3(256), 0, stream, a);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1985,9 +2005,10 @@ hipError_t launch_read_probe(const void* buf, size_t tile_bytes, const int32_t* 
                              int ntiles, uint32_t* sink, hipStream_t stream) {
   if (ntiles == 0) return hipSuccess;
   const int grid = std::min(ntiles, 4096);
-  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(buf), tile_bytes, order, ntiles, sink);
-  return hipGetLastError();
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  void* args[] = {&b, &tile_bytes, &order, &ntiles, &sink};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k_read_probe), dim3(grid), dim3(256), args,
+                         0, stream);
 }
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
@@ -2010,8 +2031,7 @@ hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
   const long long total = (long long)p.num_seqs * p.num_kv_heads * ca.row_chunks;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 255) / 256);
-  hipLaunchKernelGGL(k_cache_write, dim3(grid), dim3(256), 0, stream, ca);
-  return hipGetLastError();
+  return launch1(k_cache_write, dim3(grid), dim3(256), 0, stream, ca);
 }
 
 }  // namespace pa

@@ -165,4 +165,23 @@ def test_binding_refuses_host_tensors(lib):
     q = torch.zeros(2, 2, 64)
     with pytest.raises(ValueError):
         pa.pa_decode(q, torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
-                     torch.zeros(2, 1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+                     torch.zeros(2, 1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                     scale=0.125)
+
+
+def test_binding_requires_scale(lib):
+    """The binding computes nothing of the method: the attention scale has
+    no Python default and must be passed (the library takes it as given)."""
+    import torch
+    t = (torch.zeros(2, 2, 64), torch.zeros(4, 2, 16, 64), torch.zeros(4, 2, 16, 64),
+         torch.zeros(2, 1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        pa.pa_decode(*t)
+    with pytest.raises(TypeError):
+        pa.pa_decode_splitk(*t, partition_size=16, max_context_len=16)
+    with pytest.raises(TypeError):
+        pa.pa_decode_shared_prefix(*t, torch.zeros(2, dtype=torch.int32),
+                                   torch.zeros(1, dtype=torch.int32), 2, 16, 16)
+    import inspect
+    for f in (pa.pa_decode, pa.pa_decode_splitk, pa.pa_decode_shared_prefix):
+        assert inspect.signature(f).parameters["scale"].default is inspect.Parameter.empty

@@ -35,8 +35,10 @@ def test_bench_prints_one_json_line(args):
     rec = json.loads(lines[0])
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-                "roofline", "cpu_baseline"):
+                "roofline", "cpu_baseline", "max_abs_err", "tolerance", "pool_utilization"):
         assert key in rec, key
+    assert rec["max_abs_err"] is not None and rec["max_abs_err"] <= rec["tolerance"] == 1e-5
+    assert 0.0 < rec["pool_utilization"] <= 1.0
     assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
     assert rec["value"] > 0 and rec["ms_per_step"] > 0
     assert rec["config"]["workload"] == "tiny"
@@ -64,8 +66,15 @@ def test_cpu_baseline_record_on_the_tiny_workload():
     bench = importlib.util.module_from_spec(spec)
     sys.modules["bench_mod"] = bench          # the fork pool pickles its worker by name
     spec.loader.exec_module(bench)
+    import numpy as np
+    import oracle
     case = make_case(TINY)
-    rec = bench.cpu_baseline(case, 0.2)
+    ref, rec = bench.cpu_baseline(case, 0.2)
+    # the pass's rows, put back in sequence order, are the oracle's output
+    full = oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens,
+                         case.scale, case.block_size, case.dtype)
+    assert np.array_equal(ref, full)
+    assert np.array_equal(bench.oracle_reference(case), full)
     assert rec["kind"] == "oracle" and rec["unit"] == "KV tokens/s"
     assert rec["value"] > 0 and 1 <= rec["cores"] <= 16
     assert str(kv_token_count(case)) in rec["sample"]

@@ -199,7 +199,8 @@ def test_swap_out_and_in_keeps_decode_bitwise():
         m.vp[tb[0, t // bs], :, t % bs] = V[t]
     m.upload()
     q = dev_array(_rows(rng, 1, Hkv, d, "f16"), "f16")
-    before = host_bits(pa.pa_decode(q, m.k, m.v, dev_array(tb), dev_array(ln)))
+    scale = float(np.float32(d ** -0.5))
+    before = host_bits(pa.pa_decode(q, m.k, m.v, dev_array(tb), dev_array(ln), scale=scale))
     hk = torch.zeros((NC, Hkv, bs, d), dtype=torch.float16).pin_memory()
     hv = torch.zeros_like(hk).pin_memory()
     pa.pa_swap_blocks(hk, hv, m.k, m.v, bm.swap_out(7))
@@ -215,6 +216,6 @@ def test_swap_out_and_in_keeps_decode_bitwise():
     pa.pa_swap_blocks(m.k, m.v, hk, hv, bm.swap_in(7))
     tb2, ln2 = bm.fill_batch([7], 8)
     assert not np.array_equal(tb2[0, :5], tb[0, :5])     # different blocks
-    after = host_bits(pa.pa_decode(q, m.k, m.v, dev_array(tb2), dev_array(ln2)))
+    after = host_bits(pa.pa_decode(q, m.k, m.v, dev_array(tb2), dev_array(ln2), scale=scale))
     torch.cuda.synchronize()
     assert before.tobytes() == after.tobytes()

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import paged_kv_cache_438_amd as pa
-from synthetic import SHARED_PREFIX, Workload, make_case, small_variant, to_storage
+from synthetic import SHARED_PREFIX, make_case, small_variant, to_storage
 from tests.gpu_util import TOL, DevCase, dev_array, host_bits, host_f64, note
 
 pytestmark = pytest.mark.gpu
@@ -211,21 +211,3 @@ def test_shared_prefix_beyond_plan_lds():
     # plain split-K over the same 4200 sequences
     got = host_f64(d.decode("splitk", partition_size=16))
     _check(got, _oracle(c), w.dtype, "beyond-LDS split-K")
-
-
-def test_full_size_shared_prefix_sampled():
-    w = SHARED_PREFIX
-    c = make_case(w)
-    seq_group, prefix = _groups(c)
-    rng = np.random.default_rng(42)
-    seqs = sorted(set(rng.integers(0, w.num_seqs, 16).tolist()))
-    pairs = [(s, int(h)) for s in seqs for h in rng.choice(w.num_heads, size=3, replace=False)]
-    ref = _oracle(c, pairs=pairs)
-    d = DevCase(c)
-    for P in (256, 1024, 2048):
-        note(f"full shared: P={P} pairs={len(pairs)}")
-        got = host_f64(_run(d, c, seq_group, prefix, P))
-        torch.cuda.synchronize()
-        assert np.all(np.isfinite(got))
-        idx = tuple(np.array(pairs).T)
-        _check(got[idx], ref[idx], w.dtype, f"full shared P={P}")
