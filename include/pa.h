@@ -26,11 +26,12 @@
  *
  * Ownership and execution: every pointer argument is a DEVICE pointer owned by
  * the caller (except pa_check_inputs_host, which takes HOST pointers).  The
- * library allocates nothing and keeps no caller pointer after a call returns.
+ * library allocates nothing and keeps no caller pointer after a call returns
+ * (pa_decode_splitk_noalloc works in a static array of the library's own).
  * Every call only enqueues work on `stream` (a hipStream_t passed as void*;
  * NULL = the null stream) and returns without synchronising.  Calls are
  * thread-safe; the only global state is the calling thread's last-error
- * string.
+ * string, the per-device address of that static array, and the array.
  *
  * Errors: the host-side scalar checks below run before anything is enqueued; a
  * failing call returns a nonzero pa_status, enqueues nothing and records a
@@ -183,6 +184,36 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
                      int block_size, int max_blocks_per_seq, int num_blocks,
                      float scale, int dtype, int partition_size, int max_context_len,
                      void* workspace, size_t workspace_bytes, int flags, void* stream);
+
+/* Size of the library's static device scratch used by pa_decode_splitk_noalloc. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * pa_decode_splitk_noalloc -- pa_decode_splitk for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * must not call the allocator, harnesses that forbid it.  Same arguments,
+ * same kernels and the same result bits as pa_decode_splitk, but no
+ * workspace argument: the split-K partials and the launch plan live in a
+ * static device array of PA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library
+ * holds on each GPU it runs on until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine); on its
+ * first call on a device, with that device current, it looks up the array's
+ * device address once and keeps it.
+ *
+ * Sizes whose workspace (pa_decode_splitk_workspace_bytes) exceeds
+ * PA_NOALLOC_SCRATCH_BYTES are rejected with PA_ERR_WORKSPACE and a message
+ * naming both sizes; nothing is launched.  PA_ERR_HIP if the scratch address
+ * cannot be obtained.  All calls on one GPU share that GPU's scratch, which
+ * keeps whatever the last call left (no call needs it cleared): calls that
+ * may overlap on one GPU -- on different streams, or from different threads
+ * -- race and must be ordered by the caller.
+ */
+int pa_decode_splitk_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int num_blocks,
+                             float scale, int dtype, int partition_size, int max_context_len,
+                             int flags, void* stream);
 
 /*
  * Bytes of device workspace pa_decode_shared_prefix needs: the split-K

@@ -19,6 +19,7 @@ INCLUDE = pathlib.Path(__file__).resolve().parent.parent / "include"
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_FLAG_SHARED_KV = 1
 PA_FLAG_VALU_ONLY = 2
+PA_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/pa.h
 _DTYPES = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 _c_int, _c_void_p, _c_size_t, _c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
@@ -32,6 +33,8 @@ _SIGNATURES = {
     "pa_decode_splitk": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
                          [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
                           _c_void_p]),
+    "pa_decode_splitk_noalloc": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
+                                 [_c_float, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
     "pa_read_probe": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p, _c_void_p]),
     "pa_device_memory": (_c_int, [_c_int, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
@@ -236,6 +239,26 @@ def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                                  int(max_context_len), workspace.data_ptr(), ws_bytes,
                                  _flags(shared_kv, valu_only), _stream(q.device, stream))
     _check(st, "pa_decode_splitk")
+    return out
+
+
+def pa_decode_splitk_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                             block_tables: torch.Tensor, context_lens: torch.Tensor,
+                             partition_size: int, max_context_len: int, scale: float,
+                             out: Optional[torch.Tensor] = None, shared_kv: bool = False,
+                             valu_only: bool = False, stream=None) -> torch.Tensor:
+    """Split-K paged decode without a workspace argument: the partials live in
+    the library's static device scratch (PA_NOALLOC_SCRATCH_BYTES); for callers
+    that cannot allocate.  See pa_decode_splitk_noalloc in include/pa.h."""
+    out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
+                                                           context_lens, scale, out)
+    st = load().pa_decode_splitk_noalloc(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(),
+                                         v_pool.data_ptr(), block_tables.data_ptr(),
+                                         context_lens.data_ptr(), B, Hq, Hkv, d, bs, MB, NB,
+                                         scale, _DTYPES.get(q.dtype, -1), int(partition_size),
+                                         int(max_context_len), _flags(shared_kv, valu_only),
+                                         _stream(q.device, stream))
+    _check(st, "pa_decode_splitk_noalloc")
     return out
 
 

@@ -271,7 +271,8 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
 
 namespace {
 
-// Checks and launch of the split-K entry.
+// Checks and launch shared by the two split-K entries; `workspace` is the
+// caller's buffer or the library's static scratch.
 int splitk_checks(void* out, const void* q, const void* k_pool, const void* v_pool,
                   const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                   int num_heads, int num_kv_heads, int head_dim, int block_size,
@@ -331,6 +332,34 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
   return splitk_launch(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        dtype, partition_size, max_context_len, workspace, flags, stream);
+}
+
+int pa_decode_splitk_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                             int dtype, int partition_size, int max_context_len, int flags,
+                             void* stream) {
+  static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kNoallocScratchBytes, "scratch size");
+  int st = splitk_checks(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                         scale, dtype, partition_size, max_context_len, flags);
+  if (st) return st;
+  if (num_seqs == 0) return pa_ok();
+  const size_t need = pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                       max_context_len, partition_size);
+  if (need > PA_NOALLOC_SCRATCH_BYTES)
+    return pa_fail(PA_ERR_WORKSPACE,
+                   "these sizes need %zu bytes of split-K workspace but the static scratch holds "
+                   "%zu; use pa_decode_splitk with a caller workspace, a larger partition_size "
+                   "or fewer sequences", need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const hipError_t e = pa::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return pa_fail(PA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+  return splitk_launch(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       dtype, partition_size, max_context_len, ws, flags, stream);
 }
 
 int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,

@@ -58,6 +58,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "pa_launch.h"
@@ -1962,6 +1963,35 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     case kF16: return launch_reduce_t<kF16>(ka, p.head_dim, rgrid, stream);
     default: return launch_reduce_t<kBF16>(ka, p.head_dim, rgrid, stream);
   }
+}
+
+// Scratch for callers that cannot allocate device memory: the split-K
+// workspace of the no-allocation decode entry lives in this file-scope array.
+// Every GPU the library runs on holds its own copy, at its own address, until
+// the process ends; every call on one GPU uses that GPU's copy, so calls that
+// overlap on one GPU race.  In host code the array's name is only a stand-in
+// for the symbol: kernels and copies get the device address that
+// noalloc_scratch() looked up for the current device.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,

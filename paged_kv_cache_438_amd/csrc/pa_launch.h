@@ -75,4 +75,12 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, 
 // Single pass when p.workspace == nullptr (then p.max_partitions must be 1).
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// Size of the library's static device scratch (PA_NOALLOC_SCRATCH_BYTES in
+// pa.h), which holds the split-K workspace for callers that cannot allocate.
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+// Device address of that scratch on the current device.  The address is
+// looked up once per device (hipGetSymbolAddress, with the device current)
+// and kept; nothing is allocated.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace pa

@@ -113,6 +113,29 @@ def test_splitk_workspace_sizing_and_rejects(lib):
     assert call(flags=4, wsb=small) == 2
 
 
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """pa_decode_splitk_noalloc checks its arguments like pa_decode_splitk
+    and refuses sizes whose workspace exceeds the static scratch, all before
+    it looks up the scratch or launches anything."""
+    def call(B=64, Hq=32, Hkv=32, maxlen=100, P_=256, flags=0, out=P):
+        return lib.pa_decode_splitk_noalloc(out, P, P, P, P, P, B, Hq, Hkv, 128, 16, 2048, 9000,
+                                            0.088, 1, P_, maxlen, flags, None)
+
+    assert call(P_=24) == 2
+    assert call(maxlen=2048 * 16 + 1) == 2
+    assert call(out=0) == 1
+    assert call(flags=8) == 2
+    assert call(B=0) == 0                                   # nothing to do
+    big = dict(B=256, Hq=64, Hkv=8, maxlen=16384, P_=512)
+    need = pa.pa_decode_splitk_workspace_bytes(256, 64, 128, 16384, 512)
+    assert need > pa.PA_NOALLOC_SCRATCH_BYTES
+    assert call(**big) == 4
+    assert str(need) in pa.last_error() and "scratch" in pa.last_error()
+    # the benchmarked split-K configurations fit
+    for args in ((256, 64, 128, 16384, 8192), (16, 32, 128, 32768, 512)):
+        assert pa.pa_decode_splitk_workspace_bytes(*args) <= pa.PA_NOALLOC_SCRATCH_BYTES
+
+
 def test_shared_prefix_workspace_holds_group_tables(lib):
     """The shared-prompt workspace always holds the group tables the plan
     writes (group starts, members, prompt lengths), also for zero groups."""
@@ -180,8 +203,11 @@ def test_binding_requires_scale(lib):
     with pytest.raises(TypeError):
         pa.pa_decode_splitk(*t, partition_size=16, max_context_len=16)
     with pytest.raises(TypeError):
+        pa.pa_decode_splitk_noalloc(*t, partition_size=16, max_context_len=16)
+    with pytest.raises(TypeError):
         pa.pa_decode_shared_prefix(*t, torch.zeros(2, dtype=torch.int32),
                                    torch.zeros(1, dtype=torch.int32), 2, 16, 16)
     import inspect
-    for f in (pa.pa_decode, pa.pa_decode_splitk, pa.pa_decode_shared_prefix):
+    for f in (pa.pa_decode, pa.pa_decode_splitk, pa.pa_decode_splitk_noalloc,
+              pa.pa_decode_shared_prefix):
         assert inspect.signature(f).parameters["scale"].default is inspect.Parameter.empty
