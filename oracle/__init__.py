@@ -5,3 +5,4 @@ cpu_baseline leg import this package.  It shares no code with the HIP path.
 """
 from .paged_attention import (widen, blocks_needed, gather_kv, softmax_attention, decode,
                               decode_partitioned, cache_write, contiguous_attention)
+from .block_ops import copy_blocks, swap_blocks

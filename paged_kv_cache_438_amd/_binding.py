@@ -7,13 +7,17 @@ fallback: if libpa.so is missing or a call fails, an exception is raised.
 from __future__ import annotations
 
 import ctypes
+import os
 import pathlib
 import re
 from typing import Optional, Tuple
 
 import torch
 
-LIB_PATH = pathlib.Path(__file__).resolve().parent / "libpa.so"
+# The in-tree build; PA_LIBRARY names another build of the same sources (the
+# sanitizer build of the host code that the CPU tests load).
+LIB_PATH = pathlib.Path(os.environ.get("PA_LIBRARY") or
+                        pathlib.Path(__file__).resolve().parent / "libpa.so").resolve()
 INCLUDE = pathlib.Path(__file__).resolve().parent.parent / "include"
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2

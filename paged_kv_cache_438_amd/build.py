@@ -11,7 +11,8 @@ PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libpa.so"
-SOURCES = [CSRC / "pa_api.cpp", CSRC / "pa_block_manager.cpp", CSRC / "pa_kernels.hip"]
+SOURCES = [CSRC / "pa_api.cpp", CSRC / "pa_block_manager.cpp", CSRC / "pa_workspace.cpp",
+           CSRC / "pa_kernels.hip"]
 ARCH = "gfx950"
 
 

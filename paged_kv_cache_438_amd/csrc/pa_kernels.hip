@@ -1822,41 +1822,6 @@ hipError_t launch_reduce_t(const KArgs& ka, int d, int grid, hipStream_t st) {
 
 }  // namespace
 
-// Split-K workspace, each part starting on a 256-byte boundary:
-//   acc   [B][Hq][Pmax][D] fp32 and (m, l) [B][Hq][Pmax]
-//   plan  unit count and split count (256 bytes), units [(G + B) * Pmax] of
-//         (x, y), split sequences [B]
-//   with prompt groups: group_fill [G], group_start [G + 1], members [B],
-//   group_lp [G].
-struct WsLayout {
-  size_t ml, n_units, units, split, group_fill, group_start, members, group_lp, total;
-};
-static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
-// num_groups < 0: a plain split-K call, no group tables.
-static WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_partitions,
-                          int num_groups) {
-  const bool tables = num_groups >= 0;
-  if (num_groups < 0) num_groups = 0;
-  WsLayout w;
-  const size_t slots = (size_t)num_seqs * num_heads * max_partitions;
-  w.ml = slots * head_dim * sizeof(float);
-  w.n_units = up256(w.ml + slots * sizeof(float2));
-  w.units = w.n_units + 256;
-  w.split = up256(w.units + (size_t)(num_groups + num_seqs) * max_partitions * sizeof(int2));
-  w.group_fill = up256(w.split + (size_t)num_seqs * sizeof(int));
-  w.group_start = up256(w.group_fill + (size_t)num_groups * sizeof(int));
-  w.members = up256(w.group_start + (size_t)(num_groups + 1) * sizeof(int));
-  w.group_lp = up256(w.members + (size_t)num_seqs * sizeof(int));
-  w.total = up256(w.group_lp + (size_t)num_groups * sizeof(int));
-  if (!tables) w.total = w.group_fill;
-  return w;
-}
-
-size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions,
-                              int num_groups) {
-  return ws_layout(num_seqs, num_heads, head_dim, max_partitions, num_groups).total;
-}
-
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
   const bool shared = p.seq_group != nullptr;

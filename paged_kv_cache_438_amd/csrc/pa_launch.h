@@ -57,6 +57,12 @@ struct CacheWriteParams {
   int dtype;
 };
 
+// Byte offsets of the parts of the split-K workspace (pa_workspace.cpp).
+struct WsLayout {
+  size_t ml, n_units, units, split, group_fill, group_start, members, group_lp, total;
+};
+WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_partitions,
+                   int num_groups);
 // Byte size of the split-K workspace for these sizes: partials and plan;
 // num_groups >= 0 (shared-prompt decode) adds the group tables, -1 does not.
 size_t splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim, int max_partitions,

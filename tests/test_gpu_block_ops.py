@@ -1,7 +1,8 @@
 """GPU tests of the block operations around decode: whole-block copies
 (copy-on-write), swapping blocks to a host pool and back, and a decode loop
-driven end to end by the library's block manager, checked against a host
-mirror of the pools and the fp64 oracle."""
+driven end to end by the library's block manager, checked bit for bit
+against the oracle's block moves (oracle.copy_blocks, oracle.swap_blocks)
+and the fp64 decode oracle."""
 from __future__ import annotations
 
 import numpy as np
@@ -37,9 +38,7 @@ def test_copy_blocks_bit_exact(dtype, Hkv, bs, d):
     k, v = dev_array(kp, dtype), dev_array(vp, dtype)
     pa.pa_copy_blocks(k, v, dev_array(pairs))
     torch.cuda.synchronize()
-    ek, ev = kp.copy(), vp.copy()
-    ek[dst] = kp[src]
-    ev[dst] = vp[src]                    # the other pairs are no-ops or out of range
+    ek, ev = oracle.copy_blocks(kp, vp, pairs)   # the last four pairs move nothing
     assert host_bits(k).tobytes() == ek.tobytes()
     assert host_bits(v).tobytes() == ev.tobytes()
 
@@ -52,17 +51,16 @@ def test_swap_blocks_round_trip():
     hk = torch.zeros((NC, Hkv, bs, d), dtype=torch.float16).pin_memory()
     hv = torch.zeros_like(hk).pin_memory()
     out_pairs = [(3, 0), (4, 1), (5, 2), (9, 5)]          # a run of three, then one
+    hk0, hv0 = hk.numpy().copy(), hv.numpy().copy()
     pa.pa_swap_blocks(hk, hv, k, v, out_pairs)
     torch.cuda.synchronize()
-    for g, c in out_pairs:
-        assert hk[c].numpy().tobytes() == kp[g].tobytes()
-        assert hv[c].numpy().tobytes() == vp[g].tobytes()
+    ck, cv = oracle.swap_blocks(hk0, hv0, kp, vp, out_pairs)
+    assert hk.numpy().tobytes() == ck.tobytes()
+    assert hv.numpy().tobytes() == cv.tobytes()
     in_pairs = [(0, 12), (1, 13), (2, 14), (5, 0)]
     pa.pa_swap_blocks(k, v, hk, hv, in_pairs)
     torch.cuda.synchronize()
-    ek, ev = kp.copy(), vp.copy()
-    for (g, c), (c2, g2) in zip(out_pairs, in_pairs):
-        ek[g2], ev[g2] = kp[g], vp[g]
+    ek, ev = oracle.swap_blocks(kp, vp, ck, cv, in_pairs)
     assert host_bits(k).tobytes() == ek.tobytes()
     assert host_bits(v).tobytes() == ev.tobytes()
     with pytest.raises(pa.PaError):
@@ -85,18 +83,18 @@ def test_swap_blocks_scattered(pinned):
     g = rng.permutation(NB)[:40]
     c = rng.permutation(NC)[:40]
     note(f"swap scattered: pinned={pinned} pairs=40")
-    pa.pa_swap_blocks(hk, hv, k, v, list(zip(g.tolist(), c.tolist())))
+    out_pairs = list(zip(g.tolist(), c.tolist()))
+    pa.pa_swap_blocks(hk, hv, k, v, out_pairs)
     torch.cuda.synchronize()
-    ek = np.zeros((NC, Hkv, bs, d), dtype=np.float16)
-    ev = np.zeros_like(ek)
-    ek[c], ev[c] = kp[g], vp[g]
+    zeros = np.zeros((NC, Hkv, bs, d), dtype=np.float16)
+    ek, ev = oracle.swap_blocks(zeros, zeros, kp, vp, out_pairs)
     assert hk.numpy().tobytes() == ek.tobytes()
     assert hv.numpy().tobytes() == ev.tobytes()
     g2 = rng.permutation(NB)[:40]                          # back into other blocks
-    pa.pa_swap_blocks(k, v, hk, hv, list(zip(c.tolist(), g2.tolist())))
+    in_pairs = list(zip(c.tolist(), g2.tolist()))
+    pa.pa_swap_blocks(k, v, hk, hv, in_pairs)
     torch.cuda.synchronize()
-    fk, fv = kp.copy(), vp.copy()
-    fk[g2], fv[g2] = ek[c], ev[c]
+    fk, fv = oracle.swap_blocks(kp, vp, ek, ev, in_pairs)
     assert host_bits(k).tobytes() == fk.tobytes()
     assert host_bits(v).tobytes() == fv.tobytes()
 
@@ -153,8 +151,7 @@ def test_block_manager_driven_decode(dtype, Hq, Hkv):
                 cows.append(cow)
         if cows:
             pa.pa_copy_blocks(m.k, m.v, dev_array(np.array(cows, dtype=np.int32)))
-            for a_, b_ in cows:
-                m.kp[b_], m.vp[b_] = m.kp[a_], m.vp[a_]
+            m.kp, m.vp = oracle.copy_blocks(m.kp, m.vp, cows)
         tables, lens = bm.fill_batch(seqs, MB)
         kn, vn = _rows(rng, 4, Hkv, d, dtype), _rows(rng, 4, Hkv, d, dtype)
         pa.pa_cache_write(m.k, m.v, dev_array(kn, dtype), dev_array(vn, dtype), dev_array(tables),
