@@ -195,24 +195,33 @@ template <> __device__ __forceinline__ void store_elem<kBF16>(void* out, size_t 
   static_cast<uint16_t*>(out)[i] = f32_to_bf16_rne(v);
 }
 
-// Partition bookkeeping shared by the partition and reduce kernels.  A length
-// outside [0, max_blocks*bs], or needing more partitions than the grid holds,
-// is a contract violation: the sequence is flagged and its output set to NaN.
-struct SeqParts {
-  int len;
-  int nparts;     // ceil(len / P); 0 for an empty sequence
-  bool bad;
+// One unit of work as the split-K plan lists it (32 bytes, read with one
+// scalar load): everything a partition workgroup needs before its first
+// table lookup, so that it reaches its first K/V load in three dependent
+// memory accesses (the record, the table, the data).
+//   s      sequence (>= 0), or -(group + 1) for a partition of a group's
+//          shared prompt (sharing-aware decode)
+//   pf     partition slot in the low 24 bits, plus kUnit* flags
+//   tb, te token range [tb, te) of the unit's main stream
+//   first, cnt, lp, ts  (prompt units) the group's members in the member
+//          list, its prompt length, and a member whose table supplies the
+//          prompt's blocks
+struct __attribute__((aligned(16))) URec {
+  int s, pf, tb, te, first, cnt, lp, ts;
 };
-__device__ __forceinline__ SeqParts seq_parts(int len, int P, int max_parts, int max_blocks,
-                                              int bs_log2) {
-  SeqParts r;
-  r.bad = len < 0 || len > (max_blocks << bs_log2);
-  r.len = r.bad ? 0 : len;
-  r.nparts = (r.len + P - 1) / P;
-  if (r.nparts > max_parts) r.bad = true;
-  if (r.bad) { r.len = 0; r.nparts = 0; }
-  return r;
-}
+constexpr int kPartMask = (1 << 24) - 1;
+constexpr int kUnitDirect = 1 << 24;   // the sequence's only partition: write the output row
+constexpr int kUnitBad = 1 << 25;      // out-of-contract sequence: a NaN output row
+constexpr int kUnitTail = 1 << 26;     // a group's last prompt partition: absorbed own tokens
+// A member of a prompt group, in the group's member order (16 bytes):
+// {sequence, absorbed own tokens [y, z) (empty if none), kUnitDirect |
+// kUnitBad}.
+
+// Plan data the partition launches only read, reached through the constant
+// address space so that uniform loads of it stay scalar.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef const i32x4_t __attribute__((address_space(4)))* const_i32x4_ptr;
+typedef const int __attribute__((address_space(4)))* const_int_ptr;
 
 struct KArgs {
   void* out;
@@ -223,37 +232,37 @@ struct KArgs {
   const int32_t* lens;
   float* ws_acc;        // [B][Hq][max_parts][D]
   float2* ws_ml;        // [B][Hq][max_parts] of (max, sum)
-  const int* n_units;   // split-K plan: number of (sequence, partition) units,
-                        // then the number of sequences with several partitions
-  const int2* units;    // split-K plan: units, longest first
-  const int* split;     // split-K plan: the sequences with several partitions
-  // Shared-prompt decode (nullptr otherwise): the group of each sequence
-  // (-1: none), each group's shared prompt length, and the members of each
-  // group (members[group_start[i] .. group_start[i+1]) ).
+  const int* n_units;   // split-K plan: number of units, then of sequences to merge
+  const URec* urecs;    // split-K plan: the units, longest first (nullptr: single pass)
+  const int2* split;    // split-K plan: (sequence, partitions) of the sequences to merge
+  const int4* minfo;    // split-K plan: members of the prompt groups
+  // Sharing-aware decode, read by the plan only (nullptr otherwise): the
+  // group of each sequence (-1: none) and each group's shared prompt length.
   const int32_t* seq_group;
   const int32_t* group_prefix;
-  const int* group_start;
-  const int* members;
   int num_groups;
   int num_seqs, num_heads, num_kv_heads, bs_log2, max_blocks, num_blocks;
   int group;            // query heads per KV head
-  int chunks;           // group / GW
+  int chunks;           // column chunks (matrix cores) or head chunks (vector ALUs) per KV head
   int part_tokens;      // P
   int max_parts;
+  int grid_units;       // units one pass of the grid covers
+  int max_units;        // capacity of the unit list
   int xcd_heads;        // consecutive workgroups of a unit per XCD (xcd_group)
   float scale_log2;     // scale * log2(e)
 };
 
-// Partition layout of one sequence.  Without a prompt group, tokens [0, L)
-// are cut into partitions of P tokens.  A sequence whose group shares a
-// prompt of Lp tokens (a multiple of the block size, the same blocks at the
-// head of every member's table) has the prompt's partitions first -- they
-// are computed once for the whole group.  Its own tokens [Lp, L) follow in
-// partitions of P, unless they are few enough to be absorbed into the
-// group's last prompt partition: at most P / m tokens, where m bounds the
-// members one column chunk holds, so that partition never streams more
-// than P prompt tokens plus P own tokens.  Out-of-contract sequences get no
-// partitions and a NaN output row.
+// Partition layout of one sequence, as the plan derives it.  Without a
+// prompt group, tokens [0, L) are cut into partitions of P tokens.  A
+// sequence whose group shares a prompt of Lp tokens (a multiple of the block
+// size, the same blocks at the head of every member's table) has the
+// prompt's partitions first -- they are computed once for the whole group.
+// Its own tokens [Lp, L) follow in partitions of P, unless they are few
+// enough to be absorbed into the group's last prompt partition: at most
+// P / m tokens, where m bounds the members one column chunk holds, so that
+// partition never streams more than P prompt tokens plus P own tokens.  A
+// length outside [0, max_blocks * bs], or needing more partitions than the
+// grid holds, is a contract violation: no partitions and a NaN output row.
 struct SeqLayout {
   int len, lp, np_pre, nparts;
   bool bad, absorbed;
@@ -291,17 +300,6 @@ __device__ __forceinline__ SeqLayout layout_of(const KArgs& a, int len, int gi, 
   r.bad = bad;
   return r;
 }
-__device__ __forceinline__ SeqLayout seq_layout(const KArgs& a, int s) {
-  int gi = -1, lp = 0, cnt = 0;
-  if (a.seq_group != nullptr) {
-    gi = a.seq_group[s];
-    if (gi >= 0 && gi < a.num_groups) {
-      lp = a.group_prefix[gi];
-      cnt = a.group_start[gi + 1] - a.group_start[gi];
-    }
-  }
-  return layout_of(a, a.lens[s], gi, lp, cnt);
-}
 
 // The dispatcher hands workgroup i to XCD i % 8.  In plain order, with H
 // workgroups (KV heads x chunks) per unit, XCD x would read head tiles x,
@@ -320,6 +318,87 @@ __device__ __forceinline__ int xcd_group(int i, int H, int c) {
   return (grp / per_unit) * H + (grp % per_unit) * c + j % c;
 }
 
+// Position of a workgroup: its KV head g, chunk ch and first unit u0.
+struct WgPos {
+  int ch, g, u0;
+};
+__device__ __forceinline__ WgPos wg_pos(const KArgs& a) {
+  int wg = xcd_group(blockIdx.x, a.chunks * a.num_kv_heads, a.xcd_heads);
+  WgPos w;
+  w.ch = wg % a.chunks;  wg /= a.chunks;
+  w.g = wg % a.num_kv_heads;
+  w.u0 = wg / a.num_kv_heads;
+  return w;
+}
+
+// The units of a workgroup whose first unit is u0.  The grid covers
+// grid_units units per pass, taken in the plan's longest-first order by the
+// dispatcher; later passes go in snake order (pass 1 gives unit 2W-1-u0 to
+// workgroup u0, pass 2 unit 2W+u0, ...), so that the workgroups whose first
+// units were the shortest take the next longest.  The first record comes
+// with the unit count, which is kept; each later record is fetched while the
+// unit before it runs (prefetch(), a load into lanes 0..7 issued before that
+// unit's first K/V load, and take() after its epilogue).  Without a plan
+// (single pass) unit u0 is sequence u0, whole.
+struct UnitCursor {
+  int u0, it, n;
+  URec r;
+
+  __device__ __forceinline__ int index(int k) const {
+    const int W = grid_units_;
+    return k * W + ((k & 1) ? W - 1 - u0 : u0);
+  }
+  int grid_units_;
+
+  // The first unit; false if there is none.  PLAN: whether the launch has a
+  // unit list (split-K) or one unit per sequence (single pass).
+  template <bool PLAN>
+  __device__ __forceinline__ bool first(const KArgs& a, int u0_) {
+    u0 = u0_;
+    it = 0;
+    grid_units_ = a.grid_units;
+    if (!PLAN) {
+      n = 1;
+      const int len = a.lens[u0];
+      const bool bad = len < 0 || len > (a.max_blocks << a.bs_log2);
+      r.s = u0;
+      r.pf = kUnitDirect | (bad ? kUnitBad : 0);
+      r.tb = 0;
+      r.te = bad ? 0 : len;
+      r.first = r.cnt = r.lp = 0;
+      r.ts = u0;
+      return true;
+    }
+    n = *(const_int_ptr)a.n_units;
+    const const_i32x4_ptr rec = (const_i32x4_ptr)a.urecs + 2 * min(u0, a.max_units - 1);
+    const i32x4_t w0 = rec[0], w1 = rec[1];
+    r.s = w0.x; r.pf = w0.y; r.tb = w0.z; r.te = w0.w;
+    r.first = w1.x; r.cnt = w1.y; r.lp = w1.z; r.ts = w1.w;
+    return u0 < n;
+  }
+  // Whether the workgroup has a unit after the current one.
+  __device__ __forceinline__ bool has_next(const KArgs& a) const {
+    return a.urecs != nullptr && index(it + 1) < n;
+  }
+  // Word `lane` (< 8) of the next unit's record, loaded now.
+  __device__ __forceinline__ int prefetch(const KArgs& a, int lane) const {
+    if (!has_next(a) || lane >= 8) return 0;
+    return reinterpret_cast<const int*>(a.urecs)[8 * index(it + 1) + lane];
+  }
+  // Move to the next unit, whose record `words` holds in lanes 0..7.
+  __device__ __forceinline__ void take(int words) {
+    ++it;
+    r.s = __builtin_amdgcn_readlane(words, 0);
+    r.pf = __builtin_amdgcn_readlane(words, 1);
+    r.tb = __builtin_amdgcn_readlane(words, 2);
+    r.te = __builtin_amdgcn_readlane(words, 3);
+    r.first = __builtin_amdgcn_readlane(words, 4);
+    r.cnt = __builtin_amdgcn_readlane(words, 5);
+    r.lp = __builtin_amdgcn_readlane(words, 6);
+    r.ts = __builtin_amdgcn_readlane(words, 7);
+  }
+};
+
 // One query column of a matrix-core workgroup: whose query it is, which
 // partition slot of that sequence it fills, and whether it writes the output
 // directly (the sequence has a single partition).
@@ -327,105 +406,31 @@ struct Col {
   int seq, head, part;
   bool valid, direct, bad;
 };
-
-// The unit a matrix-core workgroup works on: KV head, chunk of 16 query
-// columns, the sequence whose table supplies the blocks, and the token range.
-// A prompt unit (prompt_group >= 0) covers one partition of a group's shared
-// prompt for all members at once: column c is member c / G, query head
-// g*G + c % G.  The last prompt partition (tail) also streams the absorbed
-// own tokens of the chunk's members.  Otherwise the columns are query heads
-// of one sequence.
-struct KUnit {
-  int ch, g, ts, t_begin, t_end, prompt_group, s, p, ncols;
-  bool bad, tail;
-};
-__device__ __forceinline__ bool resolve_kunit(const KArgs& a, KUnit& u, SeqLayout& lay) {
-  int wg = xcd_group(blockIdx.x, a.chunks * a.num_kv_heads, a.xcd_heads);
-  u.ch = wg % a.chunks;  wg /= a.chunks;
-  u.g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
-  int x = wg, y = 0;
-  if (a.units != nullptr) {
-    if (wg >= *a.n_units) return false;
-    const int2 v = a.units[wg];
-    x = v.x;
-    y = v.y;
-  }
-  u.bad = false;
-  if (x < 0) {
-    const int gi = -x - 1;
-    const int first = a.group_start[gi], cnt = a.group_start[gi + 1] - first;
-    const int lp = a.group_prefix[gi];
-    u.prompt_group = gi;
-    u.ts = a.members[first];
-    u.s = -1;
-    u.p = y;
-    u.t_begin = y * a.part_tokens;
-    u.t_end = min(u.t_begin + a.part_tokens, lp);
-    u.tail = u.t_end == lp;
-    u.ncols = min(16, cnt * a.group - u.ch * 16);
-  } else {
-    lay = seq_layout(a, x);
-    u.prompt_group = -1;
-    u.ts = u.s = x;
-    u.p = y;
-    u.bad = lay.bad;
-    u.tail = false;
-    u.t_begin = lay.lp + (y - lay.np_pre) * a.part_tokens;
-    u.t_end = min(u.t_begin + a.part_tokens, lay.len);
-    if (lay.nparts == 0) u.t_begin = u.t_end = 0;
-    u.ncols = min(16, a.group - u.ch * 16);
-  }
-  return u.ncols > 0;
-}
-__device__ __forceinline__ Col column_of(const KArgs& a, const KUnit& u, const SeqLayout& lay, int n) {
+// Column n of chunk ch of a unit: for a prompt unit, member cc / G of the
+// group at query head g*G + cc % G (cc = 16 ch + n); otherwise query head
+// g*G + cc of the unit's sequence.
+__device__ __forceinline__ Col column_of(const KArgs& a, const URec& r, int g, int ch, int ncols,
+                                         int n) {
   Col c;
-  const int cc = u.ch * 16 + n;
-  c.part = u.p;
-  if (u.prompt_group >= 0) {
-    const int first = a.group_start[u.prompt_group];
-    const int cnt = a.group_start[u.prompt_group + 1] - first;
+  const int cc = ch * 16 + n;
+  c.part = r.pf & kPartMask;
+  if (r.s < 0) {
     const int mi = cc / a.group;
-    c.valid = n < u.ncols && mi < cnt;
-    c.seq = c.valid ? a.members[first + mi] : 0;
-    c.head = u.g * a.group + cc % a.group;
-    const SeqLayout ml = seq_layout(a, c.seq);
-    c.bad = ml.bad;
-    c.valid = c.valid && !ml.bad;      // an out-of-contract member writes its NaN row itself
-    c.direct = ml.nparts == 1;
+    c.valid = n < ncols && mi < r.cnt;
+    const int4 m = c.valid ? a.minfo[r.first + mi] : make_int4(0, 0, 0, kUnitBad);
+    c.seq = m.x;
+    c.head = g * a.group + cc % a.group;
+    c.bad = (m.w & kUnitBad) != 0;
+    c.valid = c.valid && !c.bad;       // an out-of-contract member writes its NaN row itself
+    c.direct = (m.w & kUnitDirect) != 0;
   } else {
-    c.valid = n < u.ncols;
-    c.seq = u.s;
-    c.head = u.g * a.group + cc;
-    c.bad = lay.bad;
-    c.direct = lay.nparts <= 1;
+    c.valid = n < ncols;
+    c.seq = r.s;
+    c.head = g * a.group + cc;
+    c.bad = (r.pf & kUnitBad) != 0;
+    c.direct = (r.pf & kUnitDirect) != 0;
   }
   return c;
-}
-
-// The (KV head, head chunk, sequence, partition) a workgroup works on.
-// Split-K launches follow the plan written by k_plan: workgroup index
-// (unit, KV head, chunk), units longest first, so the dispatcher schedules
-// long pieces before short ones (longest-first list scheduling); workgroups
-// past the plan's unit count exit.  A single pass has one unit per sequence.
-// Either way the workgroups are dealt to the XCDs in groups of consecutive
-// heads (above).
-struct Unit {
-  int ch, g, s, p;
-};
-__device__ __forceinline__ bool resolve_unit(const KArgs& a, Unit& u) {
-  int wg = xcd_group(blockIdx.x, a.chunks * a.num_kv_heads, a.xcd_heads);
-  u.ch = wg % a.chunks;  wg /= a.chunks;
-  u.g = wg % a.num_kv_heads;  wg /= a.num_kv_heads;
-  if (a.units != nullptr) {
-    if (wg >= *a.n_units) return false;
-    const int2 su = a.units[wg];
-    u.s = su.x;
-    u.p = su.y;
-  } else {
-    u.s = wg;
-    u.p = 0;
-  }
-  return true;
 }
 
 // Software pipeline over a wave's nk steps with two register buffers: the
@@ -527,9 +532,11 @@ struct BlockIds {
 #define PA_VALU_SINGLE_WAVES 16
 #endif
 
-// One workgroup = (sequence s, KV head g, chunk of GW query heads, partition p).
-// Its W waves take the partition's 16-token steps round-robin.
-template <int DT, int D, int W, int GW, bool BIG_BLOCKS, bool NT>
+// One workgroup = (KV head g, chunk of GW query heads) of one unit per pass:
+// a whole sequence (single pass, PLAN false: one unit per workgroup), or a
+// partition of the split-K plan (PLAN true: the workgroup takes units in
+// snake order).  Its W waves take the unit's 16-token steps round-robin.
+template <int DT, int D, int W, int GW, bool BIG_BLOCKS, bool NT, bool PLAN>
 __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int ROWB = D * EB;           // bytes per token row of one head
@@ -544,185 +551,196 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
   const int r = lane / LPR;              // row group
   const int c = lane % LPR;              // 16-byte slice within the row
 
-  Unit un;
-  if (!resolve_unit(a, un)) return;
-  const int ch = un.ch, g = un.g, s = un.s, p = un.p;
-  const SeqParts sp = seq_parts(a.lens[s], a.part_tokens, a.max_parts, a.max_blocks, a.bs_log2);
-  const bool direct = sp.nparts <= 1;    // the only partition writes the output itself
-  const int t_begin = p * a.part_tokens;
-  const int t_end = min(t_begin + a.part_tokens, sp.len);
-  const int nsteps = t_end > t_begin ? (t_end - t_begin + 15) >> 4 : 0;
+  const WgPos pos = wg_pos(a);
+  const int ch = pos.ch, g = pos.g;
+  UnitCursor cur;
+  for (bool more = cur.first<PLAN>(a, pos.u0); more;) {
+    const URec ur = cur.r;
+    const int next_rec = PLAN ? cur.prefetch(a, lane) : 0;   // before this unit's first K/V load
+    const int s = ur.s, p = ur.pf & kPartMask;
+    const bool direct = (ur.pf & kUnitDirect) != 0;   // the only partition writes the output itself
+    const bool ubad = (ur.pf & kUnitBad) != 0;
+    const int t_begin = ur.tb;
+    const int t_end = ur.te;
+    const int nsteps = t_end > t_begin ? (t_end - t_begin + 15) >> 4 : 0;
 
-  const int h0 = g * a.group + ch * GW;
-  uint4 qv[GW];
+    const int h0 = g * a.group + ch * GW;
+    uint4 qv[GW];
 #pragma unroll
-  for (int hh = 0; hh < GW; ++hh)
-    qv[hh] = *reinterpret_cast<const uint4*>(
-        a.q + ((size_t)(s * a.num_heads + h0 + hh) * D) * EB + c * 16);
+    for (int hh = 0; hh < GW; ++hh)
+      qv[hh] = *reinterpret_cast<const uint4*>(
+          a.q + ((size_t)(s * a.num_heads + h0 + hh) * D) * EB + c * 16);
 
-  float m[GW], l[GW], acc[GW][EPL];
+    float m[GW], l[GW], acc[GW][EPL];
 #pragma unroll
-  for (int hh = 0; hh < GW; ++hh) {
-    m[hh] = kEmptyMax;
-    l[hh] = 0.f;
+    for (int hh = 0; hh < GW; ++hh) {
+      m[hh] = kEmptyMax;
+      l[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
-  }
-
-  const int bs_mask = (1 << a.bs_log2) - 1;
-  const size_t tile_bytes = (size_t)ROWB << a.bs_log2;          // one (block, head) tile
-  const size_t block_bytes = tile_bytes * a.num_kv_heads;
-  const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
-  bool bad_block = false;
-
-  // Iteration k of this wave handles the 16-token step starting at step_t0(k).
-  const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
-  auto step_t0 = [&](int k) { return t_begin + ((wave + k * W) << 4); };
-  BlockIds<BIG_BLOCKS, NL> ids;
-  // Fetch the block ids of step k into ids.nxt.
-  auto fetch_ids = [&](int k) {
-    const int t0 = step_t0(k);
-    if constexpr (BIG_BLOCKS) {
-      ids.nxt[0] = trow[t0 >> a.bs_log2];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) ids.nxt[i] = trow[min(t0 + i * RPL + r, t_end - 1) >> a.bs_log2];
+      for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
     }
-  };
-  struct Buf { uint4 k[NL], v[NL]; };
-  auto load_step = [&](int k, Buf& b) {
-    const int t0 = step_t0(k);
+
+    const int bs_mask = (1 << a.bs_log2) - 1;
+    const size_t tile_bytes = (size_t)ROWB << a.bs_log2;          // one (block, head) tile
+    const size_t block_bytes = tile_bytes * a.num_kv_heads;
+    const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
+    bool bad_block = false;
+
+    // Iteration k of this wave handles the 16-token step starting at step_t0(k).
+    const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+    auto step_t0 = [&](int k) { return t_begin + ((wave + k * W) << 4); };
+    BlockIds<BIG_BLOCKS, NL> ids;
+    // Fetch the block ids of step k into ids.nxt.
+    auto fetch_ids = [&](int k) {
+      const int t0 = step_t0(k);
+      if constexpr (BIG_BLOCKS) {
+        ids.nxt[0] = trow[t0 >> a.bs_log2];
+      } else {
 #pragma unroll
-    for (int i = 0; i < (BIG_BLOCKS ? 1 : NL); ++i) ids.cur[i] = ids.nxt[i];
-    fetch_ids(k + 1 < nk ? k + 1 : k);     // unconditional: no branch around loads
-    if constexpr (BIG_BLOCKS) {
-      int phys = ids.cur[0];
-      if ((unsigned)phys >= (unsigned)a.num_blocks) { bad_block = true; phys = 0; }
-      const size_t tile = (size_t)phys * block_bytes + (size_t)g * tile_bytes;
-      const uint8_t* kb = a.k_pool + tile + (size_t)(t0 & bs_mask) * ROWB + c * 16;
-      const uint8_t* vb = a.v_pool + tile + (size_t)(t0 & bs_mask) * ROWB + c * 16;
+        for (int i = 0; i < NL; ++i)
+          ids.nxt[i] = trow[min(t0 + i * RPL + r, t_end - 1) >> a.bs_log2];
+      }
+    };
+    struct Buf { uint4 k[NL], v[NL]; };
+    auto load_step = [&](int k, Buf& b) {
+      const int t0 = step_t0(k);
+#pragma unroll
+      for (int i = 0; i < (BIG_BLOCKS ? 1 : NL); ++i) ids.cur[i] = ids.nxt[i];
+      fetch_ids(k + 1 < nk ? k + 1 : k);     // unconditional: no branch around loads
+      if constexpr (BIG_BLOCKS) {
+        int phys = ids.cur[0];
+        if ((unsigned)phys >= (unsigned)a.num_blocks) { bad_block = true; phys = 0; }
+        const size_t tile = (size_t)phys * block_bytes + (size_t)g * tile_bytes;
+        const uint8_t* kb = a.k_pool + tile + (size_t)(t0 & bs_mask) * ROWB + c * 16;
+        const uint8_t* vb = a.v_pool + tile + (size_t)(t0 & bs_mask) * ROWB + c * 16;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int dt = min(i * RPL + r, t_end - 1 - t0);   // last valid row past the end
+          b.k[i] = ld16<NT>(kb + dt * ROWB);
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int dt = min(i * RPL + r, t_end - 1 - t0);
+          b.v[i] = ld16<NT>(vb + dt * ROWB);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int t = min(t0 + i * RPL + r, t_end - 1);
+          int ph = ids.cur[i];
+          if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
+          const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
+                             (size_t)(t & bs_mask) * ROWB + c * 16;
+          b.k[i] = ld16<NT>(a.k_pool + off);
+          b.v[i] = ld16<NT>(a.v_pool + off);
+        }
+      }
+    };
+    auto compute_step = [&](int k, const Buf& b) {
+      const int t0 = step_t0(k);
+      float sc[GW][NL];
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int dt = min(i * RPL + r, t_end - 1 - t0);   // last valid row past the end
-        b.k[i] = ld16<NT>(kb + dt * ROWB);
-      }
+        const bool valid = t0 + i * RPL + r < t_end;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int dt = min(i * RPL + r, t_end - 1 - t0);
-        b.v[i] = ld16<NT>(vb + dt * ROWB);
+        for (int hh = 0; hh < GW; ++hh) {
+          const float z = row_group_sum<LPR>(dot16<DT>(b.k[i], qv[hh], 0.f)) * a.scale_log2;
+          sc[hh][i] = valid ? z : -INFINITY;
+        }
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int t = min(t0 + i * RPL + r, t_end - 1);
-        int ph = ids.cur[i];
-        if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
-        const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
-                           (size_t)(t & bs_mask) * ROWB + c * 16;
-        b.k[i] = ld16<NT>(a.k_pool + off);
-        b.v[i] = ld16<NT>(a.v_pool + off);
-      }
-    }
-  };
-  auto compute_step = [&](int k, const Buf& b) {
-    const int t0 = step_t0(k);
-    float sc[GW][NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const bool valid = t0 + i * RPL + r < t_end;
 #pragma unroll
       for (int hh = 0; hh < GW; ++hh) {
-        const float z = row_group_sum<LPR>(dot16<DT>(b.k[i], qv[hh], 0.f)) * a.scale_log2;
-        sc[hh][i] = valid ? z : -INFINITY;
+        float mx = sc[hh][0];
+#pragma unroll
+        for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[hh][i]);
+        const float mn = fmaxf(m[hh], mx);
+        const float alpha = fast_exp2(m[hh] - mn);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          sc[hh][i] = fast_exp2(sc[hh][i] - mn);
+          ps += sc[hh][i];
+        }
+        l[hh] = l[hh] * alpha + ps;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
+        m[hh] = mn;
       }
-    }
 #pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
-      float mx = sc[hh][0];
+      for (int i = 0; i < NL; ++i)
 #pragma unroll
-      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[hh][i]);
-      const float mn = fmaxf(m[hh], mx);
-      const float alpha = fast_exp2(m[hh] - mn);
-      float ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        sc[hh][i] = fast_exp2(sc[hh][i] - mn);
-        ps += sc[hh][i];
-      }
-      l[hh] = l[hh] * alpha + ps;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
-      m[hh] = mn;
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-#pragma unroll
-      for (int hh = 0; hh < GW; ++hh) Axpy<DT>::run(acc[hh], sc[hh][i], b.v[i]);
-  };
+        for (int hh = 0; hh < GW; ++hh) Axpy<DT>::run(acc[hh], sc[hh][i], b.v[i]);
+    };
 
-  if (nk > 0) fetch_ids(0);
+    if (nk > 0) fetch_ids(0);
 #if PA_VALU_STAGES == 3
-  run_pipeline3<Buf>(nk, load_step, compute_step);
+    run_pipeline3<Buf>(nk, load_step, compute_step);
 #else
-  run_pipeline<Buf>(nk, load_step, compute_step);
+    run_pipeline<Buf>(nk, load_step, compute_step);
 #endif
 
-  // Merge the row groups of this wave.
+    // Merge the row groups of this wave.
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
+    for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
-      const float mo = __shfl_xor(m[hh], off);
-      const float lo = __shfl_xor(l[hh], off);
-      const float mn = fmaxf(m[hh], mo);
-      const float fa = fast_exp2(m[hh] - mn), fb = fast_exp2(mo - mn);
-      l[hh] = l[hh] * fa + lo * fb;
+      for (int hh = 0; hh < GW; ++hh) {
+        const float mo = __shfl_xor(m[hh], off);
+        const float lo = __shfl_xor(l[hh], off);
+        const float mn = fmaxf(m[hh], mo);
+        const float fa = fast_exp2(m[hh] - mn), fb = fast_exp2(mo - mn);
+        l[hh] = l[hh] * fa + lo * fb;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[hh][e] = acc[hh][e] * fa + __shfl_xor(acc[hh][e], off) * fb;
-      m[hh] = mn;
+        for (int e = 0; e < EPL; ++e)
+          acc[hh][e] = acc[hh][e] * fa + __shfl_xor(acc[hh][e], off) * fb;
+        m[hh] = mn;
+      }
     }
-  }
 
-  // Merge the waves through LDS.
-  __shared__ float s_acc[W][GW][D];
-  __shared__ float s_m[W][GW], s_l[W][GW];
-  __shared__ int s_bad;
-  if (threadIdx.x == 0) s_bad = 0;
-  __syncthreads();
-  if (bad_block) s_bad = 1;
-  if (r == 0) {
+    // Merge the waves through LDS.
+    __shared__ float s_acc[W][GW][D];
+    __shared__ float s_m[W][GW], s_l[W][GW];
+    __shared__ int s_bad;
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    if (bad_block) s_bad = 1;
+    if (r == 0) {
 #pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
+      for (int hh = 0; hh < GW; ++hh) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][hh][c * EPL + e] = acc[hh][e];
-      if (c == 0) { s_m[wave][hh] = m[hh]; s_l[wave][hh] = l[hh]; }
+        for (int e = 0; e < EPL; ++e) s_acc[wave][hh][c * EPL + e] = acc[hh][e];
+        if (c == 0) { s_m[wave][hh] = m[hh]; s_l[wave][hh] = l[hh]; }
+      }
     }
-  }
-  __syncthreads();
-  const bool poisoned = sp.bad || s_bad;
-  for (int idx = threadIdx.x; idx < GW * D; idx += W * 64) {
-    const int hh = idx / D, e = idx % D;
-    float M = s_m[0][hh];
+    __syncthreads();
+    const bool poisoned = ubad || s_bad;
+    for (int idx = threadIdx.x; idx < GW * D; idx += W * 64) {
+      const int hh = idx / D, e = idx % D;
+      float M = s_m[0][hh];
 #pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][hh]);
-    float lsum = 0.f, asum = 0.f;
+      for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][hh]);
+      float lsum = 0.f, asum = 0.f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float f = fast_exp2(s_m[w][hh] - M);
-      lsum += s_l[w][hh] * f;
-      asum += s_acc[w][hh][e] * f;
+      for (int w = 0; w < W; ++w) {
+        const float f = fast_exp2(s_m[w][hh] - M);
+        lsum += s_l[w][hh] * f;
+        asum += s_acc[w][hh][e] * f;
+      }
+      const int h = h0 + hh;
+      if (direct) {
+        float v = lsum > 0.f ? asum / lsum : 0.f;
+        if (poisoned) v = __builtin_nanf("");
+        store_elem<DT>(a.out, (size_t)(s * a.num_heads + h) * D + e, v);
+      } else {
+        const size_t slot = (size_t)(s * a.num_heads + h) * a.max_parts + p;
+        if (poisoned) { asum = __builtin_nanf(""); lsum = __builtin_nanf(""); }
+        a.ws_acc[slot * D + e] = asum;
+        if (e == 0) a.ws_ml[slot] = make_float2(M, lsum);
+      }
     }
-    const int h = h0 + hh;
-    if (direct) {
-      float v = lsum > 0.f ? asum / lsum : 0.f;
-      if (poisoned) v = __builtin_nanf("");
-      store_elem<DT>(a.out, (size_t)(s * a.num_heads + h) * D + e, v);
-    } else {
-      const size_t slot = (size_t)(s * a.num_heads + h) * a.max_parts + p;
-      if (poisoned) { asum = __builtin_nanf(""); lsum = __builtin_nanf(""); }
-      a.ws_acc[slot * D + e] = asum;
-      if (e == 0) a.ws_ml[slot] = make_float2(M, lsum);
-    }
+    if constexpr (!PLAN) break;
+    __syncthreads();                       // the merge arrays are reused by the next unit
+    more = cur.has_next(a);
+    if (more) cur.take(next_rec);
   }
 }
 
@@ -924,8 +942,11 @@ __device__ __forceinline__ int swz_pos(int c, int r) {
   else return c ^ ((r >> 1) & 7);
 }
 
-// One workgroup = (sequence s, KV head g, chunk of up to 16 query heads,
-// partition p); its W waves take the partition's 16-token steps round-robin.
+// One workgroup = (KV head g, chunk of up to 16 query columns) of one unit
+// per pass: a whole sequence (single pass), or a unit of the split-K plan
+// (a partition of a sequence, or of a group's shared prompt for all its
+// members), taken in snake order with the next unit's record prefetched.
+// Its W waves take the unit's 16-token steps round-robin.
 // Dynamic LDS: W * 4 * 16 * D * 2 bytes (two slots of K and V tiles per
 // wave), reused after the loop for the merge of the waves.
 // Occupancy the register allocation aims at: two waves per SIMD (LDS holds
@@ -946,6 +967,7 @@ void k_decode_mfma(const KArgs a) {
   constexpr int NI = D / 32;          // K (and V) operands of 16 bytes per lane per step
   constexpr int NTILE = D / 16;       // output tiles of 16 head-dim elements
   static_assert(NI * 32 == D && RPI * ROWB == 1024, "head_dim");
+  static_assert(sizeof(URec) == kUnitRecordBytes, "unit record");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -954,321 +976,342 @@ void k_decode_mfma(const KArgs a) {
   const int qa = lane & 3;            // position in the quad
   const int qb = (lane >> 2) & 3;     // quad index inside the lane group
 
-  KUnit un;
-  SeqLayout lay;
-  if (!resolve_kunit(a, un, lay)) return;
-  const int g = un.g;
-  const int nh = un.ncols;                       // columns in use in this chunk
-  const Col col = column_of(a, un, lay, n);      // this lane's column
-  uint4 qv[NI];                                  // Q^T operand, loaded below
+  const WgPos pos = wg_pos(a);
+  const int g = pos.g, ch = pos.ch;
+  UnitCursor cur;
+  for (bool more = a.urecs != nullptr ? cur.first<true>(a, pos.u0) : cur.first<false>(a, pos.u0);
+       more;) {
+    const URec ur = cur.r;
+    // The next unit's record, in flight before this unit's first K/V load (the
+    // explicit vmcnt waits below count only loads issued after it).
+    const int next_rec = cur.prefetch(a, lane);
+    const bool tail = (ur.pf & kUnitTail) != 0;
+    const int nh = min(16, (ur.s < 0 ? ur.cnt : 1) * a.group - ch * 16);   // columns in use
+    if (nh > 0) {                                  // else a chunk past this group's members
+    const bool ubad = (ur.pf & kUnitBad) != 0;
+    const int ts = ur.s < 0 ? ur.ts : ur.s;        // whose table supplies stream 0
+    const Col col = column_of(a, ur, g, ch, nh, n);   // this lane's column
+    uint4 qv[NI];                                  // Q^T operand, loaded below
 
-  // Token streams of the workgroup, 16-token steps each.  Stream 0 is the
-  // unit's token range through the table of sequence un.ts.  A group's last
-  // prompt partition adds one stream per member of the chunk, holding that
-  // member's absorbed own tokens through its own table; only that member's
-  // columns see them (the others get weight exactly 0).  Lane i describes
-  // stream i: first step, token range, sequence, member index (-1: every
-  // column).  Global step j goes to wave j % W.
-  const int cc0 = un.ch * 16;
-  const int col_mi = (cc0 + n) / a.group;        // member index of this lane's column
-  int st_first, st_tb = 0, st_te = 0, st_seq = un.ts, st_mi = -1;
-  {
-    if (lane == 0) {
-      st_tb = un.t_begin;
-      st_te = un.t_end;
-    } else if (un.tail) {
+    // Token streams of the workgroup, 16-token steps each.  Stream 0 is the
+    // unit's token range [tb, te) through the table of sequence ts.  A group's
+    // last prompt partition adds one stream per member of the chunk, holding
+    // that member's absorbed own tokens through its own table; only that
+    // member's columns see them (the others get weight exactly 0).  Lane i
+    // describes stream i: first step, token range, sequence, member index (-1:
+    // every column).  Global step j goes to wave j % W.
+    const int cc0 = ch * 16;
+    const int col_mi = (cc0 + n) / a.group;        // member index of this lane's column
+    const int cnt0 = ur.te > ur.tb ? (ur.te - ur.tb + 15) >> 4 : 0;   // steps of stream 0
+    int st_first = 0, st_tb = 0, st_te = 0, st_seq = ts, st_mi = -1;
+    int4 mrec = make_int4(ts, 0, 0, 0);
+    if (tail && lane > 0) {
       const int mi_lo = cc0 / a.group;
       const int nm = (cc0 + nh - 1) / a.group - mi_lo + 1;
       if (lane <= nm) {
-        const int first = a.group_start[un.prompt_group];
         st_mi = mi_lo + lane - 1;
-        st_seq = a.members[first + st_mi];
-        const SeqLayout ml = seq_layout(a, st_seq);
-        if (!ml.bad && ml.absorbed) {
-          st_tb = ml.lp;
-          st_te = ml.len;
+        mrec = a.minfo[ur.first + st_mi];          // in flight with the first table lookup
+      }
+    }
+    struct StepAt { int t0, t_end, mi; const_i32_ptr trow; };
+    // The stream of a step: stream 0 while the step is within it, else the
+    // highest lane whose first step is not after it (streams without steps
+    // share the next stream's first step).
+    auto step_at = [&](int k) {
+      const int j = wave + k * W;
+      StepAt r;
+      if (j < cnt0 || !tail) {
+        r.t0 = ur.tb + (j << 4);
+        r.t_end = ur.te;
+        r.mi = -1;
+        r.trow = (const_i32_ptr)(a.tables + (size_t)ts * a.max_blocks);
+      } else {
+        const uint64_t le = __builtin_amdgcn_ballot_w64(st_first <= j);
+        const int si = 63 - __builtin_clzll(le);
+        r.t0 = __builtin_amdgcn_readlane(st_tb, si) +
+               ((j - __builtin_amdgcn_readlane(st_first, si)) << 4);
+        r.t_end = __builtin_amdgcn_readlane(st_te, si);
+        r.mi = __builtin_amdgcn_readlane(st_mi, si);
+        r.trow = (const_i32_ptr)(a.tables +
+                                 (size_t)__builtin_amdgcn_readlane(st_seq, si) * a.max_blocks);
+      }
+      return r;
+    };
+    // Row of the step this lane loads with instruction j (clamped to the last
+    // valid row past the end), and its position in the slot row.
+    const int lrow = lane / LPR;
+    const int lpos = lane % LPR;
+    BlockIds<BIG_BLOCKS, NDMA> ids;
+    auto fetch_ids = [&](int k) {
+      const StepAt st = step_at(k);
+      if constexpr (BIG_BLOCKS) {
+        ids.nxt[0] = st.trow[st.t0 >> a.bs_log2];
+      } else {
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j)
+          ids.nxt[j] = st.trow[min(st.t0 + j * RPI + lrow, st.t_end - 1) >> a.bs_log2];
+      }
+    };
+    // The block ids of this wave's first step go out with the member records
+    // when the step lies in stream 0 (it needs no stream table).
+    const bool first_in0 = wave < cnt0;
+    if (first_in0) fetch_ids(0);
+    int nsteps = cnt0;
+    if (tail) {
+      if (lane == 0) {
+        st_tb = ur.tb;
+        st_te = ur.te;
+      } else if (st_mi >= 0) {
+        st_seq = mrec.x;
+        st_tb = mrec.y;                            // empty unless absorbed
+        st_te = mrec.z;
+      }
+      const int cnt = st_te > st_tb ? (st_te - st_tb + 15) >> 4 : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      st_first = incl - cnt;
+      nsteps = __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (!first_in0 && nsteps > wave) fetch_ids(0);
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+    uint8_t* wave_lds = s_dyn + wave * 2 * SLOT;
+    const uint32_t wave_lds_addr = (uint32_t)(uintptr_t)wave_lds;
+
+    f32x4_t acc[NTILE];
+#pragma unroll
+    for (int t = 0; t < NTILE; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = kEmptyMax, lsum = 0.f;
+
+    const int bs_mask = (1 << a.bs_log2) - 1;
+    const size_t tile_bytes = (size_t)ROWB << a.bs_log2;
+    const size_t block_bytes = tile_bytes * a.num_kv_heads;
+    bool bad_block = false;
+
+    const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+    auto issue = [&](int k, int slot) {
+      const StepAt st = step_at(k);
+      const int t0 = st.t0, t_end = st.t_end;
+#pragma unroll
+      for (int i = 0; i < (BIG_BLOCKS ? 1 : NDMA); ++i) ids.cur[i] = ids.nxt[i];
+      fetch_ids(k + 1 < nk ? k + 1 : k);
+      uint8_t* dst = wave_lds + slot * SLOT;
+      if constexpr (BIG_BLOCKS && PA_MFMA_BUFFER_LDS) {
+        // One block per step: buffer resources over its K and V tiles.
+        int ph = ids.cur[0];
+        if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
+        const size_t tile = (size_t)ph * block_bytes + (size_t)g * tile_bytes;
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k_pool + tile, (int)tile_bytes);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v_pool + tile, (int)tile_bytes);
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) {
+          const int row = j * RPI + lrow;
+          const int t = min(t0 + row, t_end - 1);
+          const int off = (t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
+          dma16_buf<NT>(rk, off, dst + j * 1024);
+          dma16_buf<NT>(rv, off, dst + TILE + j * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) {
+          const int row = j * RPI + lrow;
+          const int t = min(t0 + row, t_end - 1);
+          int ph = ids.cur[BIG_BLOCKS ? 0 : j];
+          if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
+          const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
+                             (size_t)(t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
+          dma16<NT>(a.k_pool + off, dst + j * 1024);
+          dma16<NT>(a.v_pool + off, dst + TILE + j * 1024);
         }
       }
-    }
-    const int cnt = st_te > st_tb ? (st_te - st_tb + 15) >> 4 : 0;
-    int incl = cnt;
+    };
+    struct Ops { uint4 k[NI], v[NI]; };
+    // Operand reads from a slot, waited for before they are returned: K of
+    // row n at chunk 4i + lg; V of row 4*lg + qa at chunk 4i + qb.
+    auto read_ops = [&](int slot) {
+      const uint32_t base = wave_lds_addr + slot * SLOT;
+      const int vr = 4 * lg + qa;
+      uint32_t ad[2 * NI];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
-    }
-    st_first = incl - cnt;
-  }
-  const int nsteps = __builtin_amdgcn_readlane(st_first + (st_te > st_tb ? (st_te - st_tb + 15) >> 4 : 0), 63);
-  struct StepAt { int t0, t_end, mi; const_i32_ptr trow; };
-  // The stream of a step is the highest lane whose first step is not after
-  // it (streams without steps share the next stream's first step).
-  auto step_at = [&](int k) {
-    const int j = wave + k * W;
-    StepAt r;
-    if (!un.tail) {
-      r.t0 = un.t_begin + (j << 4);
-      r.t_end = un.t_end;
-      r.mi = -1;
-      r.trow = (const_i32_ptr)(a.tables + (size_t)un.ts * a.max_blocks);
-    } else {
-      const uint64_t le = __builtin_amdgcn_ballot_w64(st_first <= j);
-      const int si = 63 - __builtin_clzll(le);
-      r.t0 = __builtin_amdgcn_readlane(st_tb, si) +
-             ((j - __builtin_amdgcn_readlane(st_first, si)) << 4);
-      r.t_end = __builtin_amdgcn_readlane(st_te, si);
-      r.mi = __builtin_amdgcn_readlane(st_mi, si);
-      r.trow = (const_i32_ptr)(a.tables +
-                               (size_t)__builtin_amdgcn_readlane(st_seq, si) * a.max_blocks);
-    }
-    return r;
-  };
-
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
-  uint8_t* wave_lds = s_dyn + wave * 2 * SLOT;
-  const uint32_t wave_lds_addr = (uint32_t)(uintptr_t)wave_lds;
-
-
-  f32x4_t acc[NTILE];
-#pragma unroll
-  for (int t = 0; t < NTILE; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kEmptyMax, lsum = 0.f;
-
-  const int bs_mask = (1 << a.bs_log2) - 1;
-  const size_t tile_bytes = (size_t)ROWB << a.bs_log2;
-  const size_t block_bytes = tile_bytes * a.num_kv_heads;
-  bool bad_block = false;
-
-  const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
-  // Row of the step this lane loads with instruction j (clamped to the last
-  // valid row past the end), and its position in the slot row.
-  const int lrow = lane / LPR;
-  const int lpos = lane % LPR;
-  BlockIds<BIG_BLOCKS, NDMA> ids;
-  auto fetch_ids = [&](int k) {
-    const StepAt st = step_at(k);
-    if constexpr (BIG_BLOCKS) {
-      ids.nxt[0] = st.trow[st.t0 >> a.bs_log2];
-    } else {
-#pragma unroll
-      for (int j = 0; j < NDMA; ++j)
-        ids.nxt[j] = st.trow[min(st.t0 + j * RPI + lrow, st.t_end - 1) >> a.bs_log2];
-    }
-  };
-  auto issue = [&](int k, int slot) {
-    const StepAt st = step_at(k);
-    const int t0 = st.t0, t_end = st.t_end;
-#pragma unroll
-    for (int i = 0; i < (BIG_BLOCKS ? 1 : NDMA); ++i) ids.cur[i] = ids.nxt[i];
-    fetch_ids(k + 1 < nk ? k + 1 : k);
-    uint8_t* dst = wave_lds + slot * SLOT;
-    if constexpr (BIG_BLOCKS && PA_MFMA_BUFFER_LDS) {
-      // One block per step: buffer resources over its K and V tiles.
-      int ph = ids.cur[0];
-      if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
-      const size_t tile = (size_t)ph * block_bytes + (size_t)g * tile_bytes;
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k_pool + tile, (int)tile_bytes);
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v_pool + tile, (int)tile_bytes);
-#pragma unroll
-      for (int j = 0; j < NDMA; ++j) {
-        const int row = j * RPI + lrow;
-        const int t = min(t0 + row, t_end - 1);
-        const int off = (t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
-        dma16_buf<NT>(rk, off, dst + j * 1024);
-        dma16_buf<NT>(rv, off, dst + TILE + j * 1024);
+      for (int i = 0; i < NI; ++i) {
+        ad[i] = base + n * ROWB + swz_pos<D>(4 * i + lg, n) * 16;
+        ad[NI + i] = base + TILE + vr * ROWB + swz_pos<D>(4 * i + qb, vr) * 16;
       }
-    } else {
+      u32x4_t r[2 * NI];
+      LdsReads<2 * NI>::run(r, ad);
+      Ops o;
 #pragma unroll
-      for (int j = 0; j < NDMA; ++j) {
-        const int row = j * RPI + lrow;
-        const int t = min(t0 + row, t_end - 1);
-        int ph = ids.cur[BIG_BLOCKS ? 0 : j];
-        if ((unsigned)ph >= (unsigned)a.num_blocks) { bad_block = true; ph = 0; }
-        const size_t off = (size_t)ph * block_bytes + (size_t)g * tile_bytes +
-                           (size_t)(t & bs_mask) * ROWB + swz_pos<D>(lpos, row) * 16;
-        dma16<NT>(a.k_pool + off, dst + j * 1024);
-        dma16<NT>(a.v_pool + off, dst + TILE + j * 1024);
+      for (int i = 0; i < NI; ++i) {
+        o.k[i] = make_uint4(r[i].x, r[i].y, r[i].z, r[i].w);
+        o.v[i] = make_uint4(r[NI + i].x, r[NI + i].y, r[NI + i].z, r[NI + i].w);
       }
-    }
-  };
-  struct Ops { uint4 k[NI], v[NI]; };
-  // Operand reads from a slot, waited for before they are returned: K of
-  // row n at chunk 4i + lg; V of row 4*lg + qa at chunk 4i + qb.
-  auto read_ops = [&](int slot) {
-    const uint32_t base = wave_lds_addr + slot * SLOT;
-    const int vr = 4 * lg + qa;
-    uint32_t ad[2 * NI];
+      return o;
+    };
+    auto compute_step = [&](int k, const Ops& b) {
+      const StepAt st = step_at(k);
+      const bool mine = st.mi < 0 || st.mi == col_mi;
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      ad[i] = base + n * ROWB + swz_pos<D>(4 * i + lg, n) * 16;
-      ad[NI + i] = base + TILE + vr * ROWB + swz_pos<D>(4 * i + qb, vr) * 16;
-    }
-    u32x4_t r[2 * NI];
-    LdsReads<2 * NI>::run(r, ad);
-    Ops o;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      o.k[i] = make_uint4(r[i].x, r[i].y, r[i].z, r[i].w);
-      o.v[i] = make_uint4(r[NI + i].x, r[NI + i].y, r[NI + i].z, r[NI + i].w);
-    }
-    return o;
-  };
-  auto compute_step = [&](int k, const Ops& b) {
-    const StepAt st = step_at(k);
-    const bool mine = st.mi < 0 || st.mi == col_mi;
-    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NI; ++i) sc = Mma<DT>::qk(b.k[i], qv[i], sc);
-    float z[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      z[r] = (mine && st.t0 + 4 * lg + r < st.t_end) ? sc[r] * a.scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(z[r] - mn);
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {   // wave-uniform skip
-#pragma unroll
-      for (int t = 0; t < NTILE; ++t) acc[t] *= alpha;
-    }
-    uint2 phi, plo;
-    Mma<DT>::split2(pr[0], pr[1], phi.x, plo.x);
-    Mma<DT>::split2(pr[2], pr[3], phi.y, plo.y);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      uint32_t w[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
-      quad_transpose(w, qa);
-      // tile 2i: low halves (element 2*qa of the chunk), tile 2i+1: high halves
-      const uint2 v0 = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                                  __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
-      const uint2 v1 = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
-                                  __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
-      acc[2 * i] = Mma<DT>::pv(v0, phi, acc[2 * i]);
-      acc[2 * i] = Mma<DT>::pv(v0, plo, acc[2 * i]);
-      acc[2 * i + 1] = Mma<DT>::pv(v1, phi, acc[2 * i + 1]);
-      acc[2 * i + 1] = Mma<DT>::pv(v1, plo, acc[2 * i + 1]);
-    }
-  };
-
-  // Q^T operand: column n's query row, chunk 4i + lg (zero for unused
-  // columns).  Its loads go out between the first and second slot's K/V loads,
-  // so their latency overlaps the first tile's and waiting for them (vmcnt
-  // counts in order) leaves the second slot in flight.
-  auto load_q = [&]() {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      qv[i] = make_uint4(0, 0, 0, 0);
-      if (col.valid)
-        qv[i] = *reinterpret_cast<const uint4*>(
-            a.q + ((size_t)(col.seq * a.num_heads + col.head) * D) * EB + (4 * i + lg) * 16);
-    }
-  };
-
-  // Two slots in flight; a slot is refilled as soon as its operands are in
-  // registers.
-  if (nk > 0) {
-    fetch_ids(0);
-    issue(0, 0);
-    load_q();
-    if (nk > 1) {
-      issue(1, 1);
-      wait_vmcnt<2 * NDMA>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  } else {
-    load_q();
-    wait_vmcnt<0>();
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-    asm volatile("" : "+v"(qv[i].x), "+v"(qv[i].y), "+v"(qv[i].z), "+v"(qv[i].w));
-  for (int k = 0; k < nk; ++k) {
-    const int slot = k & 1;
-    if (k + 1 < nk) wait_vmcnt<2 * NDMA>();   // the younger slot may stay in flight
-    else wait_vmcnt<0>();
-    const Ops ops = read_ops(slot);           // the slot is read: it may be refilled
-    if (k + 2 < nk) issue(k + 2, slot);
-    compute_step(k, ops);
-  }
-
-  // Sum of weights of head n over the wave's four lane groups.
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-
-  // Merge the waves through LDS (the slots are free once every wave is here:
-  // each wave's last step waited for all of its loads).
-  __syncthreads();
-  float* s_acc = reinterpret_cast<float*>(s_dyn);          // [W][nh][D]
-  float* s_m = s_acc + (size_t)W * nh * D;                // [W][16]
-  float* s_l = s_m + W * 16;                              // [W][16]
-  int* s_bad = reinterpret_cast<int*>(s_l + W * 16);
-  int* s_col = s_bad + 1;                                 // [16][4]: seq, head, part, flags
-  if (threadIdx.x == 0) *s_bad = 0;
-  if (threadIdx.x < 16) {
-    s_col[4 * n] = col.seq;
-    s_col[4 * n + 1] = col.head;
-    s_col[4 * n + 2] = col.part;
-    s_col[4 * n + 3] = (col.valid ? 1 : 0) | (col.direct ? 2 : 0) | (col.bad ? 4 : 0);
-  }
-  __syncthreads();
-  if (bad_block) *s_bad = 1;
-  if (n < nh) {
-    float* dst = s_acc + ((size_t)wave * nh + n) * D;
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NI; ++i) sc = Mma<DT>::qk(b.k[i], qv[i], sc);
+      float z[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<float2*>(dst + 32 * i + 8 * lg + 2 * r) =
-            make_float2(acc[2 * i][r], acc[2 * i + 1][r]);
-    if (lg == 0) { s_m[wave * 16 + n] = m; s_l[wave * 16 + n] = lsum; }
-  }
-  __syncthreads();
-  const bool unit_bad = un.bad || *s_bad;
-  for (int idx = threadIdx.x; idx < nh * D; idx += W * 64) {
-    const int hh = idx / D, e = idx % D;
-    const int cflags = s_col[4 * hh + 3];
-    if (!(cflags & 1)) continue;
-    const int cseq = s_col[4 * hh], chead = s_col[4 * hh + 1], cpart = s_col[4 * hh + 2];
-    const bool poisoned = unit_bad || (cflags & 4);
-    float M = s_m[hh];
+        z[r] = (mine && st.t0 + 4 * lg + r < st.t_end) ? sc[r] * a.scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      float pr[4];
 #pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w * 16 + hh]);
-    float ls = 0.f, as = 0.f;
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(z[r] - mn);
+      lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {   // wave-uniform skip
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float f = fast_exp2(s_m[w * 16 + hh] - M);
-      ls += s_l[w * 16 + hh] * f;
-      as += s_acc[((size_t)w * nh + hh) * D + e] * f;
-    }
-    if (cflags & 2) {
-      float v = ls > 0.f ? as / ls : 0.f;
-      if (poisoned) v = __builtin_nanf("");
-      store_elem<DT>(a.out, (size_t)(cseq * a.num_heads + chead) * D + e, v);
+        for (int t = 0; t < NTILE; ++t) acc[t] *= alpha;
+      }
+      uint2 phi, plo;
+      Mma<DT>::split2(pr[0], pr[1], phi.x, plo.x);
+      Mma<DT>::split2(pr[2], pr[3], phi.y, plo.y);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        uint32_t w[4] = {b.v[i].x, b.v[i].y, b.v[i].z, b.v[i].w};
+        quad_transpose(w, qa);
+        // tile 2i: low halves (element 2*qa of the chunk), tile 2i+1: high halves
+        const uint2 v0 = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                                    __builtin_amdgcn_perm(w[3], w[2], 0x05040100u));
+        const uint2 v1 = make_uint2(__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                                    __builtin_amdgcn_perm(w[3], w[2], 0x07060302u));
+        acc[2 * i] = Mma<DT>::pv(v0, phi, acc[2 * i]);
+        acc[2 * i] = Mma<DT>::pv(v0, plo, acc[2 * i]);
+        acc[2 * i + 1] = Mma<DT>::pv(v1, phi, acc[2 * i + 1]);
+        acc[2 * i + 1] = Mma<DT>::pv(v1, plo, acc[2 * i + 1]);
+      }
+    };
+
+    // Q^T operand: column n's query row, chunk 4i + lg (zero for unused
+    // columns).  Its loads go out between the first and second slot's K/V loads,
+    // so their latency overlaps the first tile's and waiting for them (vmcnt
+    // counts in order) leaves the second slot in flight.
+    auto load_q = [&]() {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        qv[i] = make_uint4(0, 0, 0, 0);
+        if (col.valid)
+          qv[i] = *reinterpret_cast<const uint4*>(
+              a.q + ((size_t)(col.seq * a.num_heads + col.head) * D) * EB + (4 * i + lg) * 16);
+      }
+    };
+
+    // Two slots in flight; a slot is refilled as soon as its operands are in
+    // registers.
+    if (nk > 0) {
+      issue(0, 0);                              // its block ids were fetched above
+      load_q();
+      if (nk > 1) {
+        issue(1, 1);
+        wait_vmcnt<2 * NDMA>();
+      } else {
+        wait_vmcnt<0>();
+      }
     } else {
-      const size_t slot = (size_t)(cseq * a.num_heads + chead) * a.max_parts + cpart;
-      if (poisoned) { as = __builtin_nanf(""); ls = __builtin_nanf(""); }
-      a.ws_acc[slot * D + e] = as;
-      if (e == 0) a.ws_ml[slot] = make_float2(M, ls);
+      load_q();
+      wait_vmcnt<0>();
     }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      asm volatile("" : "+v"(qv[i].x), "+v"(qv[i].y), "+v"(qv[i].z), "+v"(qv[i].w));
+    for (int k = 0; k < nk; ++k) {
+      const int slot = k & 1;
+      if (k + 1 < nk) wait_vmcnt<2 * NDMA>();   // the younger slot may stay in flight
+      else wait_vmcnt<0>();
+      const Ops ops = read_ops(slot);           // the slot is read: it may be refilled
+      if (k + 2 < nk) issue(k + 2, slot);
+      compute_step(k, ops);
+    }
+
+    // Sum of weights of head n over the wave's four lane groups.
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+
+    // Merge the waves through LDS (the slots are free once every wave is here:
+    // each wave's last step waited for all of its loads).
+    __syncthreads();
+    float* s_acc = reinterpret_cast<float*>(s_dyn);          // [W][nh][D]
+    float* s_m = s_acc + (size_t)W * nh * D;                // [W][16]
+    float* s_l = s_m + W * 16;                              // [W][16]
+    int* s_bad = reinterpret_cast<int*>(s_l + W * 16);
+    int* s_col = s_bad + 1;                                 // [16][4]: seq, head, part, flags
+    if (threadIdx.x == 0) *s_bad = 0;
+    if (threadIdx.x < 16) {
+      s_col[4 * n] = col.seq;
+      s_col[4 * n + 1] = col.head;
+      s_col[4 * n + 2] = col.part;
+      s_col[4 * n + 3] = (col.valid ? 1 : 0) | (col.direct ? 2 : 0) | (col.bad ? 4 : 0);
+    }
+    __syncthreads();
+    if (bad_block) *s_bad = 1;
+    if (n < nh) {
+      float* dst = s_acc + ((size_t)wave * nh + n) * D;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<float2*>(dst + 32 * i + 8 * lg + 2 * r) =
+              make_float2(acc[2 * i][r], acc[2 * i + 1][r]);
+      if (lg == 0) { s_m[wave * 16 + n] = m; s_l[wave * 16 + n] = lsum; }
+    }
+    __syncthreads();
+    const bool unit_bad = ubad || *s_bad;
+    for (int idx = threadIdx.x; idx < nh * D; idx += W * 64) {
+      const int hh = idx / D, e = idx % D;
+      const int cflags = s_col[4 * hh + 3];
+      if (!(cflags & 1)) continue;
+      const int cseq = s_col[4 * hh], chead = s_col[4 * hh + 1], cpart = s_col[4 * hh + 2];
+      const bool poisoned = unit_bad || (cflags & 4);
+      float M = s_m[hh];
+#pragma unroll
+      for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w * 16 + hh]);
+      float ls = 0.f, as = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float f = fast_exp2(s_m[w * 16 + hh] - M);
+        ls += s_l[w * 16 + hh] * f;
+        as += s_acc[((size_t)w * nh + hh) * D + e] * f;
+      }
+      if (cflags & 2) {
+        float v = ls > 0.f ? as / ls : 0.f;
+        if (poisoned) v = __builtin_nanf("");
+        store_elem<DT>(a.out, (size_t)(cseq * a.num_heads + chead) * D + e, v);
+      } else {
+        const size_t slot = (size_t)(cseq * a.num_heads + chead) * a.max_parts + cpart;
+        if (poisoned) { as = __builtin_nanf(""); ls = __builtin_nanf(""); }
+        a.ws_acc[slot * D + e] = as;
+        if (e == 0) a.ws_ml[slot] = make_float2(M, ls);
+      }
+    }
+    __syncthreads();                            // the next unit's loads refill the slots
+    }
+    more = cur.has_next(a);
+    if (more) cur.take(next_rec);
   }
 }
 
 struct PArgs {
-  KArgs k;              // sizes, lengths and (shared-prompt decode) the caller's groups
-  int* n_units;
-  int2* units;          // [(num_groups + num_seqs) * max_parts]
-  int* split;           // [num_seqs]: sequences with several partitions (n_units[1] of them)
-  int* group_fill;      // [num_groups] scratch
-  int* group_start;     // [num_groups + 1]
-  int* members;         // [num_seqs]
-  int* group_lp;        // [num_groups] prompt lengths the other launches use
+  KArgs k;              // sizes, lengths and (sharing-aware decode) the caller's groups
+  int* n_units;         // [0] units, [1] sequences with several partitions
+  URec* urecs;          // [max_units]
+  int2* split;          // [num_seqs]: (sequence, partitions) of the sequences to merge
+  int4* minfo;          // [num_seqs]: members of the groups, grouped, in sequence order
+  int* arrival;         // [num_seqs] scratch when the members do not fit in LDS
+  int* group_fill;      // [num_groups] scratch when the groups do not fit in LDS
+  int* group_start;     // [num_groups + 1] scratch, likewise
+  int* group_lp;        // [num_groups] scratch, likewise
   int max_group_size;
 };
 
@@ -1305,10 +1348,22 @@ __device__ __forceinline__ void block_exclusive_scan(const int* src, int* dst, i
   if (tid == 0) dst[n] = carry;
 }
 
-// Sequences and groups whose data the plan keeps in LDS (61 KiB in all);
-// beyond these counts it reads and writes global memory instead.
+// Sequences and groups whose data the plan keeps in LDS (about 80 KiB in
+// all); beyond these counts it reads and writes global memory instead.
 constexpr int kPlanSeqs = 4096;
 constexpr int kPlanGroups = 1024;
+// Runs of full partitions the plan queues for whole waves to write.
+constexpr int kPlanLongRuns = 256;
+
+// Record i of a run of full partitions starting with record r: partition
+// slot + i, token range shifted by i partitions.
+__device__ __forceinline__ URec run_record(const URec& r, int i, int P) {
+  URec x = r;
+  x.pf += i;
+  x.tb += i * P;
+  x.te += i * P;
+  return x;
+}
 
 // Split-K plan, one workgroup.  Every sequence contributes its own
 // partitions (at least one unit, so that empty or out-of-contract sequences
@@ -1318,15 +1373,21 @@ constexpr int kPlanGroups = 1024;
 // partition kernel's workgroups are dispatched longest first (longest-first
 // list scheduling).  The order inside a bucket depends on timing; no result
 // does, because every column's arithmetic, the streams of a unit (members
-// in ascending sequence order) and the reduce's order are fixed.
-// Lengths, groups and group tables are staged in LDS, so the phases below
-// touch global memory only to load them and to write the plan.
+// in ascending sequence order) and the reduce's order are fixed.  Each unit
+// is written as a complete record (URec), each member of a group as a
+// member record, and each sequence with several partitions as (sequence,
+// partitions) for the reduce, so the later launches never read the lengths
+// or the groups again.  Lengths, groups and group tables are staged in LDS.
 __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   __shared__ int hist[257];           // bucket counts, then starts (+ total)
   __shared__ int s_tot[kPlanThreads / 64];
   __shared__ int s_split;             // sequences with more than one partition
   __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_arr[kPlanSeqs];
   __shared__ int s_gfill[kPlanGroups], s_gstart[kPlanGroups + 1], s_glp[kPlanGroups];
+  __shared__ int s_gabs[kPlanGroups];
+  __shared__ int s_nlong;             // runs of full partitions written by whole waves
+  __shared__ URec s_lrec[kPlanLongRuns];
+  __shared__ int s_lat[kPlanLongRuns], s_ln[kPlanLongRuns];
   const int tid = threadIdx.x;
   const KArgs a = pa.k;
   const int P = a.part_tokens;
@@ -1338,7 +1399,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   int* gstart = lds_groups ? s_gstart : pa.group_start;
   int* glp = lds_groups ? s_glp : pa.group_lp;
   if (tid < 256) hist[tid] = 0;
-  if (tid == 0) s_split = 0;
+  if (tid == 0) { s_split = 0; s_nlong = 0; }
   for (int i = tid; i < NG; i += kPlanThreads) gfill[i] = 0;
   for (int s = tid; s < min(B, kPlanSeqs); s += kPlanThreads) {
     s_len[s] = a.lens[s];
@@ -1357,6 +1418,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     }
     return layout_of(a, len_of(s), gi, lp, cnt);
   };
+  int* arrival = s_arr;
+  int* gabs = lds_groups ? s_gabs : pa.group_fill;   // reuses the member counts' scratch
   if (shared) {
     // Members of each group, grouped by a counting sort.
     for (int s = tid; s < B; s += kPlanThreads) {
@@ -1382,40 +1445,39 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     __syncthreads();
     // Members in ascending sequence order, so which member's own tokens a
     // workgroup streams at which step does not depend on timing: first in
-    // arrival order, then each placed at its rank among its group's members.
+    // arrival order, then each placed at its rank among its group's members
+    // with its record: sequence, absorbed own tokens, flags.
     const int nmem = gstart[NG];
-    int* arrival = nmem <= kPlanSeqs ? s_arr : reinterpret_cast<int*>(pa.units);
+    if (nmem > kPlanSeqs) arrival = pa.arrival;
     for (int s = tid; s < B; s += kPlanThreads) {
       const int gi = grp_of(s);
       if (gi >= 0 && gi < NG) arrival[gstart[gi] + atomicAdd(&gfill[gi], 1)] = s;
     }
     __syncthreads();
+    for (int i = tid; i < NG; i += kPlanThreads) gabs[i] = 0;
+    __syncthreads();
+    // gabs[gi] <- absorbed own tokens of the group per column chunk (at most
+    // about P by the absorption bound), summed while the records are written.
     for (int x = tid; x < nmem; x += kPlanThreads) {
       const int s = arrival[x];
       const int gi = grp_of(s);
       const int lo = gstart[gi], hi = gstart[gi + 1];
       int rank = 0;
       for (int y = lo; y < hi; ++y) rank += arrival[y] < s;
-      pa.members[lo + rank] = s;
-    }
-    for (int i = tid; i < NG; i += kPlanThreads) gfill[i] = 0;
-    __syncthreads();
-    // gfill[gi] <- absorbed own tokens of the group per column chunk (at
-    // most about P by the absorption bound).
-    for (int s = tid; s < B; s += kPlanThreads) {
       const SeqLayout ml = layout(s);
-      if (ml.bad || !ml.absorbed) continue;
-      const int gi = grp_of(s);
-      const int cnt = gstart[gi + 1] - gstart[gi];
-      atomicAdd(&gfill[gi], (ml.len - ml.lp) / ((cnt * a.group + 15) / 16));
+      const bool own = ml.absorbed && !ml.bad;
+      pa.minfo[lo + rank] = make_int4(s, own ? ml.lp : 0, own ? ml.len : 0,
+                                      (ml.nparts == 1 ? kUnitDirect : 0) | (ml.bad ? kUnitBad : 0));
+      if (own) atomicAdd(&gabs[gi], (ml.len - ml.lp) / (((hi - lo) * a.group + 15) / 16));
     }
     __syncthreads();
   }
   // Units hold up to 2P tokens (a last prompt partition with absorbed own
   // tokens); buckets split [0, 2P] evenly, largest first.
+  const float bucket_scale = 128.f / (float)P;
   auto bucket = [&](int size) {
-    const long long b = ((long long)(2 * P - size) * 256) / (2 * P);
-    return (int)(b < 0 ? 0 : (b > 255 ? 255 : b));
+    const int b = (int)((float)(2 * P - size) * bucket_scale);   // only the order depends on it
+    return b < 0 ? 0 : (b > 255 ? 255 : b);
   };
   // Prompt partitions of a group: np_pre units, the last holding the rest.
   auto prompt_parts = [&](int gi) {
@@ -1425,35 +1487,81 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     return (lp + P - 1) / P;
   };
   for (int pass = 0; pass < 2; ++pass) {
-    // pass 0 counts units per size bucket, pass 1 places them.  put() takes
-    // n consecutive partitions y0 .. y0+n-1 of one size with one atomic.
-    auto put = [&](int size, int x, int y0, int n) {
+    // pass 0 counts units per size bucket, pass 1 writes them.  put() takes
+    // a run of n partitions of one size with one atomic: record i of the
+    // run is `r` with partition slot + i and token range shifted by i * P.
+    auto put = [&](int size, const URec& r, int n) {
       if (n <= 0) return;
       const int b = bucket(size);
       if (pass == 0) {
         atomicAdd(&hist[b], n);
-      } else {
-        const int at = atomicAdd(&hist[b], n);
-        for (int i = 0; i < n; ++i) pa.units[at + i] = make_int2(x, y0 + i);
+        return;
       }
+      const int at = atomicAdd(&hist[b], n);
+      if (n > 2) {                     // a longer run: queued for a whole wave
+        const int li = atomicAdd(&s_nlong, 1);
+        if (li < kPlanLongRuns) {
+          s_lrec[li] = r;
+          s_lat[li] = at;
+          s_ln[li] = n;
+          return;
+        }
+      }
+      for (int i = 0; i < n; ++i) pa.urecs[at + i] = run_record(r, i, P);
     };
     for (int gi = tid; gi < NG; gi += kPlanThreads) {
       const int np = prompt_parts(gi);
-      put(P, -(gi + 1), 0, np - 1);
+      if (np == 0) continue;
+      URec r;
+      r.s = -(gi + 1);
+      r.first = gstart[gi];
+      r.cnt = gstart[gi + 1] - r.first;
+      r.lp = glp[gi];
+      r.ts = arrival[r.first];                   // any member: all share the prompt's blocks
+      r.pf = 0;
+      r.tb = 0;
+      r.te = P;
+      put(P, r, np - 1);
       // the last partition: the rest of the prompt plus absorbed own tokens
-      if (np > 0) put(glp[gi] - (np - 1) * P + gfill[gi], -(gi + 1), np - 1, 1);
+      r.pf = (np - 1) | kUnitTail;
+      r.tb = (np - 1) * P;
+      r.te = r.lp;
+      put(r.lp - r.tb + gabs[gi], r, 1);
     }
     for (int s = tid; s < B; s += kPlanThreads) {
       const SeqLayout lay = layout(s);
       const int own = lay.nparts - lay.np_pre;
-      if (pass == 0 && lay.nparts > 1) pa.split[atomicAdd(&s_split, 1)] = s;
-      if (lay.nparts == 0) put(0, s, 0, 1);
+      if (pass == 0 && lay.nparts > 1) pa.split[atomicAdd(&s_split, 1)] = make_int2(s, lay.nparts);
+      URec r;
+      r.s = s;
+      r.first = r.cnt = r.lp = 0;
+      r.ts = s;
+      if (lay.nparts == 0) {                     // empty or out of contract: one empty unit
+        r.pf = kUnitDirect | (lay.bad ? kUnitBad : 0);
+        r.tb = r.te = 0;
+        put(0, r, 1);
+      }
       if (own > 0) {
-        put(P, s, lay.np_pre, own - 1);                       // full partitions
-        put(lay.len - lay.lp - (own - 1) * P, s, lay.np_pre + own - 1, 1);
+        const int flags = lay.nparts == 1 ? kUnitDirect : 0;
+        r.pf = lay.np_pre | flags;
+        r.tb = lay.lp;
+        r.te = lay.lp + P;
+        put(P, r, own - 1);                      // full partitions
+        r.pf = (lay.np_pre + own - 1) | flags;
+        r.tb = lay.lp + (own - 1) * P;
+        r.te = lay.len;
+        put(lay.len - r.tb, r, 1);
       }
     }
     __syncthreads();
+    if (pass == 1) {
+      // The queued runs: one wave per run, lane i writing records i, i + 64,
+      // ... (consecutive records: coalesced stores).
+      const int nl = min(s_nlong, kPlanLongRuns);
+      for (int li = tid >> 6; li < nl; li += kPlanThreads / 64)
+        for (int i = tid & 63; i < s_ln[li]; i += 64)
+          pa.urecs[s_lat[li] + i] = run_record(s_lrec[li], i, P);
+    }
     if (pass == 0) {
       // bucket counts -> bucket starts; hist[256] = number of units
       block_exclusive_scan(hist, hist, 256, s_tot);
@@ -1464,11 +1572,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       }
       __syncthreads();
     }
-  }
-  // The group tables the partition and reduce launches read.
-  if (shared && lds_groups) {
-    for (int i = tid; i <= NG; i += kPlanThreads) pa.group_start[i] = gstart[i];
-    for (int i = tid; i < NG; i += kPlanThreads) pa.group_lp[i] = glp[i];
   }
 }
 
@@ -1498,10 +1601,9 @@ __global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
   const int lane = threadIdx.x & 63;
   const int total = a.n_units[1] * a.num_heads;
   for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < total; it += gridDim.x * 4) {
-    const int s = a.split[it / a.num_heads];
-    const int item = s * a.num_heads + it % a.num_heads;
-    const SeqLayout lay = seq_layout(a, s);
-    const int np = lay.nparts;
+    const int2 sp = a.split[it / a.num_heads];   // (sequence, partitions)
+    const int item = sp.x * a.num_heads + it % a.num_heads;
+    const int np = sp.y;
     const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
     const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
 
@@ -1731,32 +1833,47 @@ hipError_t launch1(void (*kernel)(A), dim3 grid, dim3 block, size_t lds, hipStre
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, st);
 }
 
-template <int DT, int D, int W, int GW>
+constexpr size_t kOneWorkgroupPerCuLds = 81 * 1024;
+
+template <int DT, int D, int W, int GW, bool PLAN>
 hipError_t launch_decode_t(const KArgs& ka, bool big, bool nt, int grid, hipStream_t st) {
   const dim3 gd(grid), bd(W * 64);
-  if (big && nt) return launch1(k_decode<DT, D, W, GW, true, true>, gd, bd, 0, st, ka);
-  if (big) return launch1(k_decode<DT, D, W, GW, true, false>, gd, bd, 0, st, ka);
-  if (nt) return launch1(k_decode<DT, D, W, GW, false, true>, gd, bd, 0, st, ka);
-  return launch1(k_decode<DT, D, W, GW, false, false>, gd, bd, 0, st, ka);
+  // Split-K partitions of 512 tokens or more run one 8-wave workgroup per CU
+  // (measured faster than two on the long-context batch): the unused dynamic
+  // LDS below is over half of a CU's 160 KiB, so a second one does not fit.
+  const size_t lds = (W == 8 && PLAN) ? kOneWorkgroupPerCuLds : 0;
+  if (big && nt) return launch1(k_decode<DT, D, W, GW, true, true, PLAN>, gd, bd, lds, st, ka);
+  if (big) return launch1(k_decode<DT, D, W, GW, true, false, PLAN>, gd, bd, lds, st, ka);
+  if (nt) return launch1(k_decode<DT, D, W, GW, false, true, PLAN>, gd, bd, lds, st, ka);
+  return launch1(k_decode<DT, D, W, GW, false, false, PLAN>, gd, bd, lds, st, ka);
 }
 
-// Waves per workgroup: 16 only for one query head per wave and rows of at
-// most 256 bytes (the two register buffers then fit in 128 VGPRs), else 8 or 4.
+// Waves per workgroup: a single pass uses 16 for one query head per wave
+// and rows of at most 256 bytes (the two register buffers then fit in 128
+// VGPRs), else 8; split-K uses 8 for partitions of 512 tokens or more, else 4.
 template <int DT, int D>
 hipError_t dispatch_gw(const KArgs& ka, int gw, int waves, bool big, bool nt, int grid,
                        hipStream_t st) {
+  if (ka.urecs == nullptr) {
+    switch (gw) {
+      case 1:
+        if constexpr (D * Elem<DT>::bytes <= 256)
+          if (waves >= 16) return launch_decode_t<DT, D, 16, 1, false>(ka, big, nt, grid, st);
+        return launch_decode_t<DT, D, 8, 1, false>(ka, big, nt, grid, st);
+      case 2: return launch_decode_t<DT, D, 8, 2, false>(ka, big, nt, grid, st);
+      default: return launch_decode_t<DT, D, 8, 4, false>(ka, big, nt, grid, st);
+    }
+  }
   switch (gw) {
     case 1:
-      if constexpr (D * Elem<DT>::bytes <= 256)
-        if (waves >= 16) return launch_decode_t<DT, D, 16, 1>(ka, big, nt, grid, st);
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 1>(ka, big, nt, grid, st);
-      return launch_decode_t<DT, D, 4, 1>(ka, big, nt, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 1, true>(ka, big, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 1, true>(ka, big, nt, grid, st);
     case 2:
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 2>(ka, big, nt, grid, st);
-      return launch_decode_t<DT, D, 4, 2>(ka, big, nt, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 2, true>(ka, big, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 2, true>(ka, big, nt, grid, st);
     default:
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 4>(ka, big, nt, grid, st);
-      return launch_decode_t<DT, D, 4, 4>(ka, big, nt, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 4, true>(ka, big, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 4, true>(ka, big, nt, grid, st);
   }
 }
 
@@ -1790,6 +1907,11 @@ hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t ld
 
 #ifndef PA_REDUCE_MAX_WGS
 #define PA_REDUCE_MAX_WGS 1024
+#endif
+
+// Most workgroups a split-K partition launch starts (see launch_decode).
+#ifndef PA_MAX_GRID_WGS
+#define PA_MAX_GRID_WGS 4096
 #endif
 
 // Smallest query-head group sent to the matrix-core kernel.
@@ -1838,14 +1960,14 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.ws_acc = p.workspace;
   ka.ws_ml = ws ? reinterpret_cast<float2*>(ws + wl.ml) : nullptr;
   ka.n_units = ws ? reinterpret_cast<const int*>(ws + wl.n_units) : nullptr;
-  ka.units = ws ? reinterpret_cast<const int2*>(ws + wl.units) : nullptr;
-  ka.split = ws ? reinterpret_cast<const int*>(ws + wl.split) : nullptr;
-  // The partition and reduce launches read the plan's copies of the groups.
+  ka.urecs = ws ? reinterpret_cast<const URec*>(ws + wl.units) : nullptr;
+  ka.split = ws ? reinterpret_cast<const int2*>(ws + wl.split) : nullptr;
+  ka.minfo = shared ? reinterpret_cast<const int4*>(ws + wl.minfo) : nullptr;
+  // The caller's groups: read by the plan only.
   ka.seq_group = shared ? p.seq_group : nullptr;
-  ka.group_prefix = shared ? reinterpret_cast<const int32_t*>(ws + wl.group_lp) : nullptr;
-  ka.group_start = shared ? reinterpret_cast<const int*>(ws + wl.group_start) : nullptr;
-  ka.members = shared ? reinterpret_cast<const int*>(ws + wl.members) : nullptr;
+  ka.group_prefix = shared ? p.group_prefix : nullptr;
   ka.num_groups = shared ? p.num_groups : 0;
+  ka.max_units = (int)wl.max_units;
   ka.num_seqs = p.num_seqs;
   ka.num_heads = p.num_heads;
   ka.num_kv_heads = p.num_kv_heads;
@@ -1876,11 +1998,21 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int row_bytes = p.head_dim * (p.dtype == kF32 ? 4 : 2);
   if (p.workspace == nullptr) waves = gw == 1 && row_bytes <= 256 ? PA_VALU_SINGLE_WAVES : 8;
   else waves = p.partition_size >= 512 ? PA_SPLIT_WAVES : 4;
-  const long long units = p.workspace == nullptr
-                              ? p.num_seqs
-                              : (long long)(p.num_seqs + (shared ? p.num_groups : 0)) * p.max_partitions;
-  const long long grid = (long long)ka.chunks * p.num_kv_heads * units;
-  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // One pass of the grid covers grid_units units: every sequence without a
+  // plan; with one, the unit list's capacity, capped at PA_MAX_GRID_WGS
+  // workgroups (the workgroups then take further units in snake order), so
+  // that few workgroups find no unit when the plan lists far fewer units
+  // than the capacity bound.
+  const long long H = (long long)ka.chunks * p.num_kv_heads;
+  long long units = p.num_seqs;
+  if (ws != nullptr) {
+    units = (long long)wl.max_units;
+    units = std::min(units, std::max(1LL, (long long)PA_MAX_GRID_WGS / H));
+  }
+  ka.grid_units = (int)units;
+  const long long grid = H * units;
+  if (grid <= 0 || grid > 0x7fffffffLL || wl.max_units > 0x7fffffffULL)
+    return hipErrorInvalidConfiguration;
   // Heads per XCD group: the largest power of two c with c tiles of one
   // (block, KV head) within PA_XCD_GROUP_BYTES, c dividing the workgroups of
   // a unit and 8c dividing the grid (so the renumbering is a bijection).
@@ -1897,13 +2029,13 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (ws != nullptr) {
     PArgs pa_;
     pa_.k = ka;
-    pa_.k.group_prefix = p.group_prefix;       // the caller's prompt lengths
     pa_.n_units = reinterpret_cast<int*>(ws + wl.n_units);
-    pa_.units = reinterpret_cast<int2*>(ws + wl.units);
-    pa_.split = reinterpret_cast<int*>(ws + wl.split);
+    pa_.urecs = reinterpret_cast<URec*>(ws + wl.units);
+    pa_.split = reinterpret_cast<int2*>(ws + wl.split);
+    pa_.minfo = shared ? reinterpret_cast<int4*>(ws + wl.minfo) : nullptr;
+    pa_.arrival = shared ? reinterpret_cast<int*>(ws + wl.arrival) : nullptr;
     pa_.group_fill = shared ? reinterpret_cast<int*>(ws + wl.group_fill) : nullptr;
     pa_.group_start = shared ? reinterpret_cast<int*>(ws + wl.group_start) : nullptr;
-    pa_.members = shared ? reinterpret_cast<int*>(ws + wl.members) : nullptr;
     pa_.group_lp = shared ? reinterpret_cast<int*>(ws + wl.group_lp) : nullptr;
     pa_.max_group_size = p.max_group_size;
     e = launch1(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, pa_);

@@ -59,8 +59,11 @@ struct CacheWriteParams {
 
 // Byte offsets of the parts of the split-K workspace (pa_workspace.cpp).
 struct WsLayout {
-  size_t ml, n_units, units, split, group_fill, group_start, members, group_lp, total;
+  size_t max_units;   // capacity of the unit list
+  size_t ml, n_units, units, split, minfo, arrival, group_fill, group_start, group_lp, total;
 };
+// Bytes of one unit record of the plan.
+constexpr size_t kUnitRecordBytes = 32;
 WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_partitions,
                    int num_groups);
 // Byte size of the split-K workspace for these sizes: partials and plan;

@@ -91,8 +91,8 @@ def test_splitk_workspace_sizing_and_rejects(lib):
     need = pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 256)
     up = lambda x: (x + 255) // 256 * 256
     partials = up(64 * 32 * 8 * (128 + 2) * 4)
-    plan = up(256 + 64 * 8 * 8)              # counts, then one (seq, part) pair each
-    split = up(64 * 4)                       # the sequences with several partitions
+    plan = up(256 + 64 * 8 * 32)             # counts, then a 32-byte record per (seq, part)
+    split = up(64 * 8)                       # (sequence, partitions) of the split sequences
     assert need == partials + plan + split
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 2048, 24) == 0
     assert pa.pa_decode_splitk_workspace_bytes(64, 32, 96, 2048, 256) == 0
@@ -137,19 +137,21 @@ def test_noalloc_rejects_before_touching_the_device(lib):
 
 
 def test_shared_prefix_workspace_holds_group_tables(lib):
-    """The shared-prompt workspace always holds the group tables the plan
-    writes (group starts, members, prompt lengths), also for zero groups."""
+    """The shared-prompt workspace always holds the member records and the
+    plan's group scratch (arrival order, counts, starts, prompt lengths),
+    also for zero groups."""
     up = lambda x: (x + 255) // 256 * 256
     B, H, d, maxlen, P = 64, 32, 128, 2048, 256
     parts = maxlen // P + 1                   # one more than the plain split
     for G in (0, 5):
         slots = B * H * parts
         n_units = up(slots * d * 4 + slots * 8)
-        split = up(n_units + 256 + (G + B) * parts * 8)
-        group_fill = up(split + B * 4)
+        split = up(n_units + 256 + (G + B) * parts * 32)
+        minfo = up(split + B * 8)
+        arrival = up(minfo + B * 16)
+        group_fill = up(arrival + B * 4)
         group_start = up(group_fill + G * 4)
-        members = up(group_start + (G + 1) * 4)
-        group_lp = up(members + B * 4)
+        group_lp = up(group_start + (G + 1) * 4)
         total = up(group_lp + G * 4)
         assert pa.pa_decode_shared_prefix_workspace_bytes(B, H, d, maxlen, P, G) == total, G
     assert pa.pa_decode_shared_prefix_workspace_bytes(B, H, d, maxlen, P, -1) == 0

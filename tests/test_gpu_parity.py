@@ -341,3 +341,42 @@ def test_api_errors_on_device():
         pa.pa_decode_splitk(d.q, d.k_pool, d.v_pool, d.tables, d.lens, partition_size=16,
                             max_context_len=49, scale=float(c.scale))   # > max_blocks * bs
     assert e.value.status == 2
+
+
+# ------------------------------------------------------------------ several units per workgroup
+# Split-K launches start at most 4096 workgroups; with more (unit, head)
+# pairs than that, each workgroup takes further units in snake order and
+# prefetches the next unit's record while the current one runs.  These
+# shapes have 6k-27k (unit, head) workgroup slots at 16-token partitions.
+MANY_UNITS = [
+    # (name, B, Hq, Hkv, d, bs, dtype, length range)
+    ("valu_mha_f16", 64, 32, 32, 128, 16, "f16", (100, 320)),
+    ("valu_f32_d64", 48, 16, 16, 64, 8, "f32", (1, 260)),
+    ("mfma_gqa_bf16", 64, 64, 8, 128, 16, "bf16", (16, 400)),
+    ("mfma_gqa_f16_g4_bs4", 128, 16, 4, 64, 4, "f16", (0, 300)),
+]
+
+
+@pytest.mark.parametrize("spec", MANY_UNITS, ids=lambda s: s[0])
+def test_several_units_per_workgroup(spec):
+    name, B, Hq, Hkv, d, bs, dtype, (lo, hi) = spec
+    rng = np.random.default_rng(31)
+    lens = tuple(int(x) for x in rng.integers(lo, hi + 1, size=B))
+    w = edge_workload(name, lens, Hq, Hkv, d, bs, dtype, 16, seed=23)
+    c = make_case(w)
+    ref = _oracle(c)
+    d_ = DevCase(c)
+    units = sum(-(-L // 16) for L in lens)
+    note(f"several units: {name} B={B} units={units} (x {Hkv} KV heads) lens {min(lens)}..{max(lens)}")
+    first = None
+    for P in (16, 32):
+        got = d_.decode("splitk", P)
+        torch.cuda.synchronize()
+        _check_close(host_f64(got), ref, dtype, f"{name}/splitk/{P}")
+        if P == 16:
+            first = host_bits(got).tobytes()
+    again = host_bits(d_.decode("splitk", 16)).tobytes()
+    assert again == first, "rerun differs"
+    for s_, L in enumerate(lens):
+        if L == 0:
+            assert np.all(host_f64(got)[s_] == 0.0)

@@ -211,3 +211,26 @@ def test_shared_prefix_beyond_plan_lds():
     # plain split-K over the same 4200 sequences
     got = host_f64(d.decode("splitk", partition_size=16))
     _check(got, _oracle(c), w.dtype, "beyond-LDS split-K")
+
+
+def test_shared_prefix_several_units_per_workgroup():
+    """Enough groups and 16-token partitions that the launch's 4096
+    workgroups each take several prompt and own units (snake order, the next
+    record prefetched), with absorbed and non-absorbed members mixed."""
+    w = SMALL.replace(name="shared_many_units", num_seqs=96, groups=24, group_size=4,
+                      prompt_len=64, length_lo=1, length_hi=40, num_heads=32, num_kv_heads=32,
+                      head_dim=128, max_blocks_per_seq=8)
+    c = make_case(w)
+    seq_group, prefix = _groups(c)
+    seq_group[[3, 50]] = -1
+    d = DevCase(c)
+    ref = _oracle(c)
+    outs = []
+    for P in (16, 32):
+        note(f"shared several units: B=96 groups=24 P={P}")
+        got = _run(d, c, seq_group, prefix, P)
+        torch.cuda.synchronize()
+        _check(host_f64(got), ref, w.dtype, f"shared several units P={P}")
+        outs.append(host_bits(got).tobytes())
+    assert host_bits(_run(d, c, seq_group, prefix, 16)).tobytes() == outs[0]
+
