@@ -217,6 +217,18 @@ constexpr int kUnitTail = 1 << 26;     // a group's last prompt partition: absor
 // {sequence, absorbed own tokens [y, z) (empty if none), kUnitDirect |
 // kUnitBad}.
 
+// Unsigned division by a divisor d fixed at launch, for numerators below
+// 2^31: with l = ceil(log2 d) and m = ceil(2^(31+l) / d), floor(x / d) =
+// (x * m) >> (31 + l) (the rounding error of m stays below 1/d for such x).
+// The host fills it (set_divisor).
+struct Divisor {
+  uint32_t m;
+  int shift;
+  __device__ __forceinline__ int div(int x) const {
+    return (int)(((uint64_t)(uint32_t)x * m) >> shift);
+  }
+};
+
 // Plan data the partition launches only read, reached through the constant
 // address space so that uniform loads of it stay scalar.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -245,6 +257,8 @@ struct KArgs {
   int group;            // query heads per KV head
   int chunks;           // column chunks (matrix cores) or head chunks (vector ALUs) per KV head
   int part_tokens;      // P
+  Divisor part_div;     // division by P
+  int members_chunk;    // most members one column chunk of 16 holds
   int max_parts;
   int grid_units;       // units one pass of the grid covers
   int max_units;        // capacity of the unit list
@@ -267,14 +281,12 @@ struct SeqLayout {
   int len, lp, np_pre, nparts;
   bool bad, absorbed;
 };
-// Most members whose query columns share one chunk of 16 (a member has
-// `group` consecutive columns).
-__device__ __forceinline__ int members_per_chunk(int group) {
-  return 16 % group == 0 ? 16 / group : 16 / group + 2;
-}
 // Layout from a sequence's length and group (-1: none); for a group in
-// range, lp_g is its prompt length and cnt its member count.
-__device__ __forceinline__ SeqLayout layout_of(const KArgs& a, int len, int gi, int lp_g, int cnt) {
+// range, lp_g is its prompt length and cnt its member count.  absorb_max[m]
+// = P / max(1, m) for m <= members_chunk, the most own tokens a member may
+// bring to its group's last prompt partition.
+__device__ __forceinline__ SeqLayout layout_of(const KArgs& a, int len, int gi, int lp_g, int cnt,
+                                               const int* absorb_max) {
   SeqLayout r;
   r.len = len;
   r.lp = 0;
@@ -286,12 +298,9 @@ __device__ __forceinline__ SeqLayout layout_of(const KArgs& a, int len, int gi, 
     if (r.lp < 0 || r.lp > r.len || (r.lp & ((1 << a.bs_log2) - 1)) != 0) bad = true;
   }
   if (bad) { r.len = 0; r.lp = 0; }
-  r.np_pre = (r.lp + a.part_tokens - 1) / a.part_tokens;
-  if (r.lp > 0) {
-    const int m = max(1, min(cnt, members_per_chunk(a.group)));
-    r.absorbed = r.len - r.lp <= a.part_tokens / m;
-  }
-  r.nparts = r.np_pre + (r.absorbed ? 0 : (r.len - r.lp + a.part_tokens - 1) / a.part_tokens);
+  r.np_pre = a.part_div.div(r.lp + a.part_tokens - 1);
+  if (r.lp > 0) r.absorbed = r.len - r.lp <= absorb_max[min(cnt, a.members_chunk)];
+  r.nparts = r.np_pre + (r.absorbed ? 0 : a.part_div.div(r.len - r.lp + a.part_tokens - 1));
   if (r.nparts > a.max_parts) {
     bad = true;
     r.len = r.lp = r.np_pre = r.nparts = 0;
@@ -1308,7 +1317,7 @@ struct PArgs {
   URec* urecs;          // [max_units]
   int2* split;          // [num_seqs]: (sequence, partitions) of the sequences to merge
   int4* minfo;          // [num_seqs]: members of the groups, grouped, in sequence order
-  int* arrival;         // [num_seqs] scratch when the members do not fit in LDS
+  int* arrival;         // [2 num_seqs] scratch when the members do not fit in LDS
   int* group_fill;      // [num_groups] scratch when the groups do not fit in LDS
   int* group_start;     // [num_groups + 1] scratch, likewise
   int* group_lp;        // [num_groups] scratch, likewise
@@ -1382,9 +1391,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   __shared__ int hist[257];           // bucket counts, then starts (+ total)
   __shared__ int s_tot[kPlanThreads / 64];
   __shared__ int s_split;             // sequences with more than one partition
-  __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_arr[kPlanSeqs];
+  __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_arr[kPlanSeqs], s_mem[kPlanSeqs];
   __shared__ int s_gfill[kPlanGroups], s_gstart[kPlanGroups + 1], s_glp[kPlanGroups];
   __shared__ int s_gabs[kPlanGroups];
+  __shared__ int s_absorb[17];        // P / max(1, m), m = 0 .. 16
   __shared__ int s_nlong;             // runs of full partitions written by whole waves
   __shared__ URec s_lrec[kPlanLongRuns];
   __shared__ int s_lat[kPlanLongRuns], s_ln[kPlanLongRuns];
@@ -1400,6 +1410,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   int* glp = lds_groups ? s_glp : pa.group_lp;
   if (tid < 256) hist[tid] = 0;
   if (tid == 0) { s_split = 0; s_nlong = 0; }
+  if (tid <= 16) s_absorb[tid] = P / max(1, tid);
   for (int i = tid; i < NG; i += kPlanThreads) gfill[i] = 0;
   for (int s = tid; s < min(B, kPlanSeqs); s += kPlanThreads) {
     s_len[s] = a.lens[s];
@@ -1416,15 +1427,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       lp = glp[gi];
       cnt = gstart[gi + 1] - gstart[gi];
     }
-    return layout_of(a, len_of(s), gi, lp, cnt);
+    return layout_of(a, len_of(s), gi, lp, cnt, s_absorb);
   };
-  int* arrival = s_arr;
+  int* arrival = s_mem;                // members in arrival order (prompt groups)
   int* gabs = lds_groups ? s_gabs : pa.group_fill;   // reuses the member counts' scratch
   if (shared) {
-    // Members of each group, grouped by a counting sort.
+    // Members of each group, grouped by a counting sort; each sequence keeps
+    // the slot its atomic gave it (arrival order).
     for (int s = tid; s < B; s += kPlanThreads) {
       const int gi = grp_of(s);
-      if (gi >= 0 && gi < NG) atomicAdd(&gfill[gi], 1);
+      const int slot = gi >= 0 && gi < NG ? atomicAdd(&gfill[gi], 1) : -1;
+      if (s < kPlanSeqs) s_arr[s] = slot;
+      else pa.arrival[s] = slot;
     }
     __syncthreads();
     block_exclusive_scan(gfill, gstart, NG, s_tot);
@@ -1440,21 +1454,19 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
                       lp <= (a.max_blocks << a.bs_log2) &&
                       (lp & ((1 << a.bs_log2) - 1)) == 0 && (lp + P - 1) / P <= a.max_parts;
       glp[i] = ok ? lp : -1;
-      gfill[i] = 0;
+      gabs[i] = 0;
     }
-    __syncthreads();
     // Members in ascending sequence order, so which member's own tokens a
     // workgroup streams at which step does not depend on timing: first in
-    // arrival order, then each placed at its rank among its group's members
-    // with its record: sequence, absorbed own tokens, flags.
+    // arrival order (mem), then each placed at its rank among its group's
+    // members with its record: sequence, absorbed own tokens, flags.
     const int nmem = gstart[NG];
-    if (nmem > kPlanSeqs) arrival = pa.arrival;
+    int* mem = nmem <= kPlanSeqs ? s_mem : pa.arrival + B;
     for (int s = tid; s < B; s += kPlanThreads) {
       const int gi = grp_of(s);
-      if (gi >= 0 && gi < NG) arrival[gstart[gi] + atomicAdd(&gfill[gi], 1)] = s;
+      if (gi >= 0 && gi < NG) mem[gstart[gi] + (s < kPlanSeqs ? s_arr[s] : pa.arrival[s])] = s;
     }
-    __syncthreads();
-    for (int i = tid; i < NG; i += kPlanThreads) gabs[i] = 0;
+    arrival = mem;
     __syncthreads();
     // gabs[gi] <- absorbed own tokens of the group per column chunk (at most
     // about P by the absorption bound), summed while the records are written.
@@ -1824,6 +1836,14 @@ int ilog2(int x) {
   return r;
 }
 
+Divisor set_divisor(int d) {
+  const int l = ilog2(d);
+  Divisor v;
+  v.m = (uint32_t)((((uint64_t)1 << (31 + l)) + (uint64_t)d - 1) / (uint64_t)d);
+  v.shift = 31 + l;
+  return v;
+}
+
 // Launch a kernel that takes one argument struct and return the status of
 // this launch alone (not an error some earlier runtime call left behind).
 template <typename A>
@@ -1986,6 +2006,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int cols = shared ? ka.group * (p.max_group_size > 1 ? p.max_group_size : 1) : ka.group;
   ka.chunks = mfma ? (cols + 15) / 16 : ka.group / gw;
   ka.part_tokens = p.partition_size;
+  ka.part_div = set_divisor(std::max(1, p.partition_size));
+  ka.members_chunk = 16 % ka.group == 0 ? 16 / ka.group : 16 / ka.group + 2;
   ka.max_parts = p.max_partitions;
   ka.scale_log2 = p.scale * kLog2e;
   // Streaming (non-temporal) K/V loads unless blocks are shared.

@@ -149,7 +149,7 @@ def test_shared_prefix_workspace_holds_group_tables(lib):
         split = up(n_units + 256 + (G + B) * parts * 32)
         minfo = up(split + B * 8)
         arrival = up(minfo + B * 16)
-        group_fill = up(arrival + B * 4)
+        group_fill = up(arrival + B * 8)
         group_start = up(group_fill + G * 4)
         group_lp = up(group_start + (G + 1) * 4)
         total = up(group_lp + G * 4)
