@@ -24,7 +24,8 @@ import numpy as np
 ROOT = pathlib.Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
-from synthetic import WORKLOADS, algorithmic_bytes, kv_token_count, make_case  # noqa: E402
+from synthetic import (WORKLOADS, algorithmic_bytes, contiguous_cache, kv_token_count,  # noqa: E402
+                       make_case)
 
 HBM_PEAK_GBS = 8000.0
 # Max-abs error bounds against the fp64 oracle, fp32 accumulation.
@@ -39,7 +40,7 @@ DEFAULT_ENTRY = {"llama2_7b": ("single", None), "long_bs512": ("splitk", 512),
                  "gqa_70b": ("splitk", 8192), "shared_prefix": ("shared", 2048),
                  "tiny": ("single", None)}
 ENTRY_NAME = {"single": "pa_decode", "splitk": "pa_decode_splitk",
-              "shared": "pa_decode_shared_prefix"}
+              "shared": "pa_decode_shared_prefix", "contiguous": "pa_decode_contiguous"}
 
 
 def log(*a):
@@ -315,8 +316,16 @@ def main() -> int:
     ap.add_argument("--block-size", type=int, default=None,
                     help="override the workload's block size (page-size sweep)")
     ap.add_argument("--contiguous", action="store_true",
-                    help="one block per sequence, as long as the longest possible sequence: "
-                         "the contiguous per-sequence cache the pages contrast paging with")
+                    help="decode over a contiguous cache that reserves the workload's longest "
+                         "possible context for every sequence, with no block table "
+                         "(pa_decode_contiguous): the scheme the pages contrast paging with")
+    ap.add_argument("--through-table", action="store_true",
+                    help="with --contiguous: the paged entry over the same contiguous memory, "
+                         "seen as one block per sequence through an identity table (isolates "
+                         "the cost of the table lookups)")
+    ap.add_argument("--one-block", action="store_true",
+                    help="paged decode with one block per sequence, as long as the longest "
+                         "possible sequence")
     ap.add_argument("--cached", action="store_true",
                     help="plain cached K/V loads (the shared-blocks policy) even without sharing")
     ap.add_argument("--valu-only", action="store_true",
@@ -358,13 +367,21 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     entry, P = DEFAULT_ENTRY[w.name]
-    if args.contiguous or args.block_size:
-        longest = w.length_hi if w.length_kind != "shared_prefix" else w.prompt_len + w.length_hi
-        if w.length_kind == "fixed":
-            longest = max(w.lengths)
+    longest = w.length_hi if w.length_kind != "shared_prefix" else w.prompt_len + w.length_hi
+    if w.length_kind == "fixed":
+        longest = max(w.lengths)
+    if args.contiguous and (args.block_size or args.one_block or args.entry == "shared" or
+                            (not args.entry and entry == "shared")):
+        raise SystemExit("--contiguous runs the single-pass or split-K decode over its own "
+                         "cache: no --block-size, --one-block or shared-prompt entry")
+    if args.through_table and not (args.contiguous and longest & (longest - 1) == 0 and
+                                   longest <= 65536):
+        raise SystemExit("--through-table needs --contiguous and a longest context that is a "
+                         "power of two of at most 65536 (a valid block size)")
+    if args.one_block or args.block_size:
         bs = args.block_size or 1 << (longest - 1).bit_length()
-        if args.contiguous and bs < longest:
-            raise SystemExit("--contiguous needs a block at least as long as the longest sequence")
+        if args.one_block and bs < longest:
+            raise SystemExit("--one-block needs a block at least as long as the longest sequence")
         if w.length_kind == "shared_prefix" and w.prompt_len % bs:
             raise SystemExit("the shared prompt must be whole blocks")
         w = w.replace(block_size=bs, max_blocks_per_seq=-(-longest // bs))
@@ -374,7 +391,7 @@ def main() -> int:
     elif args.partition:
         P = args.partition
     t = time.perf_counter()
-    case = make_case(w, seed=args.seed)
+    case = make_case(w, seed=args.seed, keep_logical=args.contiguous)
     log(f"bench: generated {w.name} seed={case.seed} in {time.perf_counter() - t:.1f} s; "
         f"sum L = {kv_token_count(case)}, pool blocks = {case.num_blocks}")
 
@@ -399,15 +416,26 @@ def main() -> int:
         return torch.from_numpy(a).to(dev)
 
     dt = case.dtype
-    q, kp, vp = d(case.q, dt), d(case.k_pool, dt), d(case.v_pool, dt)
-    kn, vn = d(case.k_new, dt), d(case.v_new, dt)
+    q = d(case.q, dt)
     tb, ln = d(case.block_tables), d(case.context_lens)
+    if args.contiguous:
+        # Every sequence reserves the longest context the workload allows.
+        kc, vc = contiguous_cache(case, longest, device=dev)
+        case.logical_k = case.logical_v = None
+        # The same memory as a pool of one block per sequence, block s for
+        # sequence s.
+        ident = torch.arange(w.num_seqs, dtype=torch.int32, device=dev).reshape(-1, 1)
+    else:
+        kp, vp = d(case.k_pool, dt), d(case.v_pool, dt)
+        kn, vn = d(case.k_new, dt), d(case.v_new, dt)
     out = torch.empty_like(q)
     maxlen = int(case.context_lens.max())
     scale = float(case.scale)
     ws = None
     if entry == "splitk":
-        need = pa.pa_decode_splitk_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, maxlen, P)
+        # A contiguous call bounds the partitions by its region length.
+        bound = longest if args.contiguous else maxlen
+        need = pa.pa_decode_splitk_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim, bound, P)
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     if entry == "shared":
         if case.shared_groups is None:
@@ -428,7 +456,15 @@ def main() -> int:
     shared = args.cached or (case.shared_groups is not None and entry != "shared")
 
     def decode():
-        if entry == "single":
+        if args.through_table and entry == "single":
+            pa.pa_decode(q, kc, vc, ident, ln, scale=scale, out=out, valu_only=args.valu_only)
+        elif args.through_table:
+            pa.pa_decode_splitk(q, kc, vc, ident, ln, partition_size=P, max_context_len=longest,
+                                scale=scale, out=out, workspace=ws, valu_only=args.valu_only)
+        elif args.contiguous:
+            pa.pa_decode_contiguous(q, kc, vc, ln, scale=scale, partition_size=P or 0, out=out,
+                                    workspace=ws, valu_only=args.valu_only)
+        elif entry == "single":
             pa.pa_decode(q, kp, vp, tb, ln, scale=scale, out=out, shared_kv=shared,
                          valu_only=args.valu_only)
         elif entry == "shared":
@@ -440,8 +476,14 @@ def main() -> int:
                                 scale=scale, out=out, workspace=ws, shared_kv=shared,
                                 valu_only=args.valu_only)
 
+    # A step is the new token's cache write and the decode; a contiguous
+    # cache has no paged write, so its step is the decode alone.
+    def write():
+        if not args.contiguous:
+            pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
+
     def step():
-        pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
+        write()
         decode()
 
     for _ in range(args.warmup):
@@ -453,7 +495,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
+        write()
         evs[i][0].record()
         decode()
         evs[i][1].record()
@@ -465,9 +507,17 @@ def main() -> int:
     e = w.elem_bytes
     # With prompt groups the blocks a group shares are counted once (unique
     # bytes, what HBM must deliver); the per-sequence sum is reported beside.
-    dec_bytes = algorithmic_bytes(case, unique=case.shared_groups is not None)
-    logical_bytes = algorithmic_bytes(case)
-    cw_bytes = 4 * w.num_seqs * w.num_kv_heads * w.head_dim * e + 4 * 2 * w.num_seqs
+    # Table entries count only where a table is read (one per sequence
+    # through the identity table).
+    tables_read = not args.contiguous or args.through_table
+    dec_bytes = algorithmic_bytes(case, unique=case.shared_groups is not None,
+                                  tables=tables_read and not args.through_table)
+    logical_bytes = algorithmic_bytes(case, tables=tables_read and not args.through_table)
+    if args.through_table:
+        dec_bytes += 4 * w.num_seqs
+        logical_bytes += 4 * w.num_seqs
+    cw_bytes = 0 if args.contiguous else \
+        4 * w.num_seqs * w.num_kv_heads * w.head_dim * e + 4 * 2 * w.num_seqs
     step_bytes = dec_bytes + cw_bytes
     ms_step = elapsed * 1e3 / K
     value = step_bytes * K / elapsed / 1e9
@@ -490,7 +540,8 @@ def main() -> int:
         ceiling["decode_frac_of_best_read"] = round(achieved / best, 4)
 
     traffic = None
-    tf = ROOT / "profiles" / f"traffic_{w.name}_{entry}.json"
+    entry_key = entry if args.through_table else "contiguous" if args.contiguous else entry
+    tf = ROOT / "profiles" / f"traffic_{w.name}_{entry_key}.json"
     if tf.exists():
         try:
             rec = json.loads(tf.read_text())
@@ -501,7 +552,7 @@ def main() -> int:
 
     mfma = entry == "shared" or (dt != "f32" and w.group_ratio >= 2 and not args.valu_only)
     kname = "k_decode_mfma" if mfma else "k_decode"
-    kernel = kname if entry == "single" else f"k_plan + {kname} (partitions) + k_reduce"
+    kernel = kname if not P else f"k_plan + {kname} (partitions) + k_reduce"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -516,18 +567,27 @@ def main() -> int:
         "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[dt],
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "seed": case.seed,
-                   "block_size": w.block_size,
-                   "entry": ENTRY_NAME[entry],
+                   "block_size": longest if args.through_table else None if args.contiguous
+                   else w.block_size,
+                   "max_len": longest if args.contiguous else None,
+                   "entry": ENTRY_NAME[entry_key],
                    "partition_size": P, "accumulate": "f32", "shared_kv_flag": shared,
                    "valu_only": bool(args.valu_only),
                    "global_batch": w.num_seqs, "kv_tokens": tokens,
-                   "step": "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
+                   "kv_layout": ("contiguous cache through an identity table"
+                                 if args.through_table else "contiguous cache"
+                                 if args.contiguous else "paged pool"),
+                   "step": "decode (contiguous cache, no paged write)" if args.contiguous
+                   else "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
         "max_abs_err": max_err,
         "tolerance": tol,
         "check": ("output of the last timed step vs the fp64 oracle, all "
                   f"{w.num_seqs * w.num_heads} (sequence, head) rows") if ref is not None
                  else "skipped (--no-check)",
-        "pool_utilization": round(case.unique_blocks / case.num_blocks, 4),
+        # Share of the reserved KV memory that holds tokens: used blocks over
+        # the pool, or tokens over the rows a contiguous cache reserves.
+        "pool_utilization": round(tokens / (w.num_seqs * longest) if args.contiguous
+                                  else case.unique_blocks / case.num_blocks, 4),
         "kv_tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

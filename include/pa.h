@@ -150,10 +150,10 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
  * Bytes of device workspace pa_decode_splitk needs for these sizes: fp32
  * partial results for num_seqs * num_heads * ceil(max_context_len /
  * partition_size) partitions, each head_dim accumulators plus a running
- * maximum and sum, then the launch plan (256 bytes of counts, one 8-byte
- * entry per possible (sequence, partition) pair, and 4 bytes per sequence
- * for the list of sequences with several partitions), each part rounded up
- * to 256 bytes.  Returns 0 for invalid sizes.
+ * maximum and sum, then the launch plan (256 bytes of counts, one 32-byte
+ * unit record per possible (sequence, partition) pair, and 8 bytes per
+ * sequence for the list of sequences with several partitions), each part
+ * rounded up to 256 bytes.  Returns 0 for invalid sizes.
  */
 size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_dim,
                                         int max_context_len, int partition_size);
@@ -218,8 +218,10 @@ int pa_decode_splitk_noalloc(void* out, const void* q, const void* k_pool, const
 /*
  * Bytes of device workspace pa_decode_shared_prefix needs: the split-K
  * partials for ceil(max_context_len / partition_size) + 1 partitions per
- * sequence, the launch plan, and the group tables (about 16 bytes per group
- * and 4 per sequence).  Returns 0 for invalid sizes.
+ * sequence, the launch plan (its unit records also cover every group's
+ * prompt partitions), and the group tables (a 16-byte member record and 8
+ * bytes of plan scratch per sequence, 12 bytes per group).  Returns 0 for
+ * invalid sizes.
  */
 size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int head_dim,
                                                int max_context_len, int partition_size,
@@ -274,6 +276,40 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
                             int dtype, int num_groups, int max_group_size, int partition_size,
                             int max_context_len, void* workspace, size_t workspace_bytes,
                             int flags, void* stream);
+
+/*
+ * pa_decode_contiguous -- the same decode attention over a contiguous KV
+ * cache: the scheme paging replaces, in which every request reserves room for
+ * the longest context it may reach ("IO-5 vLLM Paged Attention", section 1,
+ * the contiguous KV problem; "vLLM's efficiency secret: PagedAttention and
+ * dynamic memory management", section "KV cache like virtual memory", whose
+ * example reserves the maximum context for every request).  It is here to
+ * measure what the block-table indirection costs:
+ * the kernels are those of pa_decode and pa_decode_splitk with the table
+ * lookup removed, so for the same rows the result is the same bits as the
+ * paged call (paging does not change the attention: "IO-5 vLLM Paged
+ * Attention", "5 common misconceptions").
+ *
+ * k_cache and v_cache are [num_seqs][num_kv_heads][max_len][head_dim]: row t
+ * of KV head g of sequence s is k_cache[s][g][t].  out[s][h] =
+ * softmax(q[s][h] . K_s^T * scale) V_s over rows 0 .. L-1, L =
+ * context_lens[s]; rows past L are never read and may hold anything.
+ * Accumulation, rounding, L = 0 and the NaN row for 0 <= L <= max_len
+ * broken are as for pa_decode.  max_len * head_dim * element size must not
+ * exceed 2^31 - 1 bytes.
+ *
+ * partition_size 0: one pass, as pa_decode; `workspace` is not used (may be
+ * NULL).  Otherwise the split-K launches of pa_decode_splitk with
+ * max_context_len = max_len and a workspace of
+ * pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim, max_len,
+ * partition_size) bytes.  `flags`: 0 or PA_FLAG_VALU_ONLY (a contiguous
+ * cache holds no shared rows, so PA_FLAG_SHARED_KV is rejected).
+ */
+int pa_decode_contiguous(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* context_lens, int num_seqs, int num_heads,
+                         int num_kv_heads, int head_dim, int max_len, float scale, int dtype,
+                         int partition_size, void* workspace, size_t workspace_bytes, int flags,
+                         void* stream);
 
 /*
  * pa_copy_blocks -- copy whole blocks of both pools, every KV head:

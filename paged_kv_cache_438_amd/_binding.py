@@ -39,6 +39,9 @@ _SIGNATURES = {
                           _c_void_p]),
     "pa_decode_splitk_noalloc": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
                                  [_c_float, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
+    "pa_decode_contiguous": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 +
+                             [_c_float, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
+                              _c_void_p]),
     "pa_read_probe": (_c_int, [_c_void_p, _c_size_t, _c_void_p, _c_int, _c_void_p, _c_void_p]),
     "pa_device_memory": (_c_int, [_c_int, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "pa_check_inputs_host": (_c_int, [_c_void_p, _c_void_p] + [_c_int] * 5 +
@@ -263,6 +266,53 @@ def pa_decode_splitk_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torc
                                          int(max_context_len), _flags(shared_kv, valu_only),
                                          _stream(q.device, stream))
     _check(st, "pa_decode_splitk_noalloc")
+    return out
+
+
+def pa_decode_contiguous(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         context_lens: torch.Tensor, scale: float, partition_size: int = 0,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, valu_only: bool = False,
+                         stream=None) -> torch.Tensor:
+    """Decode attention over a contiguous cache, k_cache and v_cache
+    [num_seqs][num_kv_heads][max_len][head_dim], with no block table:
+    ``partition_size`` 0 for one pass, else split-K with that partition.
+    See pa_decode_contiguous in include/pa.h."""
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, n)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be "
+                         "[num_seqs][num_kv_heads][max_len][head_dim]")
+    B, Hkv, max_len, d = k_cache.shape
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != d:
+        raise ValueError("q must be [num_seqs][num_heads][head_dim] with k_cache's num_seqs "
+                         "and head_dim")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the caches must share one dtype")
+    _dev(context_lens, "context_lens", torch.int32)
+    if context_lens.shape != (B,):
+        raise ValueError("context_lens must be [num_seqs]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if scale is None:
+        raise TypeError("scale is required (usually 1/sqrt(head_dim), as an fp32 value)")
+    Hq = q.shape[1]
+    ws_ptr, ws_bytes = None, 0
+    if partition_size:
+        need = pa_decode_splitk_workspace_bytes(B, Hq, d, max_len, partition_size)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = load().pa_decode_contiguous(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, d,
+                                     max_len, float(scale), _DTYPES.get(q.dtype, -1),
+                                     int(partition_size), ws_ptr, ws_bytes,
+                                     _flags(False, valu_only), _stream(q.device, stream))
+    _check(st, "pa_decode_contiguous")
     return out
 
 

@@ -106,6 +106,7 @@ pa::DecodeParams make_params(void* out, const void* q, const void* k_pool, const
   p.partition_size = 0;
   p.max_partitions = 1;
   p.flags = flags;
+  p.max_len = 0;
   p.seq_group = nullptr;
   p.group_prefix = nullptr;
   p.num_groups = 0;
@@ -360,6 +361,51 @@ int pa_decode_splitk_noalloc(void* out, const void* q, const void* k_pool, const
   return splitk_launch(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        dtype, partition_size, max_context_len, ws, flags, stream);
+}
+
+int pa_decode_contiguous(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* context_lens, int num_seqs, int num_heads,
+                         int num_kv_heads, int head_dim, int max_len, float scale, int dtype,
+                         int partition_size, void* workspace, size_t workspace_bytes, int flags,
+                         void* stream) {
+  if (max_len <= 0) return pa_fail(PA_ERR_INVALID_ARG, "max_len must be > 0 (got %d)", max_len);
+  if (flags & PA_FLAG_SHARED_KV)
+    return pa_fail(PA_ERR_INVALID_ARG, "PA_FLAG_SHARED_KV does not apply to a contiguous cache");
+  // The checks of a paged call whose one block per sequence holds max_len
+  // rows (block_size 1 stands in for the size, which need not be a power of
+  // two); the table pointer is not used.
+  int st = check_decode(out, q, k_cache, v_cache, context_lens, context_lens, num_seqs,
+                        num_heads, num_kv_heads, head_dim, 1, max_len, num_seqs > 0 ? num_seqs : 1,
+                        scale, dtype, flags);
+  if (st) return st;
+  if ((int64_t)max_len * head_dim * (dtype == PA_F32 ? 4 : 2) > 0x7fffffffLL)
+    return pa_fail(PA_ERR_UNSUPPORTED, "max_len %d: one sequence's rows of a KV head exceed 2 GiB",
+                   max_len);
+  if (partition_size < 0 || partition_size % 16 != 0)
+    return pa_fail(PA_ERR_INVALID_ARG,
+                   "partition_size must be 0 (single pass) or a positive multiple of 16 (got %d)",
+                   partition_size);
+  if (num_seqs == 0) return pa_ok();
+  pa::DecodeParams p = make_params(out, q, k_cache, v_cache, nullptr, context_lens, num_seqs,
+                                   num_heads, num_kv_heads, head_dim, 1, 1, num_seqs, scale,
+                                   dtype, flags);
+  p.max_len = max_len;
+  if (partition_size == 0) {
+    p.partition_size = (int)(ceil_div64(max_len, 16) * 16);
+    p.max_partitions = 1;
+  } else {
+    const size_t need = pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim, max_len,
+                                                         partition_size);
+    if (!workspace || workspace_bytes < need)
+      return pa_fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+                     workspace_bytes, workspace ? "" : ", NULL");
+    if (!aligned16(workspace))
+      return pa_fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    p.partition_size = partition_size;
+    p.max_partitions = (int)ceil_div64(max_len, partition_size);
+    p.workspace = static_cast<float*>(workspace);
+  }
+  return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
 int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int num_pairs,

@@ -254,6 +254,7 @@ struct KArgs {
   const int32_t* group_prefix;
   int num_groups;
   int num_seqs, num_heads, num_kv_heads, bs_log2, max_blocks, num_blocks;
+  int max_len;          // longest valid context: max_blocks << bs_log2, or a contiguous cache's rows
   int group;            // query heads per KV head
   int chunks;           // column chunks (matrix cores) or head chunks (vector ALUs) per KV head
   int part_tokens;      // P
@@ -291,7 +292,7 @@ __device__ __forceinline__ SeqLayout layout_of(const KArgs& a, int len, int gi, 
   r.len = len;
   r.lp = 0;
   r.absorbed = false;
-  bool bad = r.len < 0 || r.len > (a.max_blocks << a.bs_log2);
+  bool bad = r.len < 0 || r.len > a.max_len;
   if (a.seq_group != nullptr) {
     if (gi >= a.num_groups || gi < -1) bad = true;
     else if (gi >= 0) r.lp = lp_g;
@@ -369,7 +370,7 @@ struct UnitCursor {
     if (!PLAN) {
       n = 1;
       const int len = a.lens[u0];
-      const bool bad = len < 0 || len > (a.max_blocks << a.bs_log2);
+      const bool bad = len < 0 || len > a.max_len;
       r.s = u0;
       r.pf = kUnitDirect | (bad ? kUnitBad : 0);
       r.tb = 0;
@@ -521,6 +522,17 @@ __device__ __forceinline__ void run_pipeline3(int nk, LoadF&& load, ComputeF&& c
   }
 }
 
+// Where the decode kernels find token t of sequence s, KV head g:
+//  - kSmallPages: blocks of fewer than 16 tokens; row t % bs of block
+//    table[s][t / bs], looked up for every row;
+//  - kBigPages: blocks of 16 tokens or more, so a 16-token step lies in one
+//    block, looked up once per step;
+//  - kContiguous: no table; row t of a region of max_len rows that sequence
+//    s owns per KV head, [num_seqs][num_kv_heads][max_len][head_dim] -- the
+//    preallocated contiguous cache that paging replaces.  The "block" of
+//    every step is the sequence itself.
+enum KvLayout { kSmallPages = 0, kBigPages = 1, kContiguous = 2 };
+
 // Block ids of the steps a wave walks, fetched one step ahead of their use.
 // Blocks of at least 16 tokens: a 16-token step lies in one block, whose id is
 // a wave-uniform scalar load.  Smaller blocks: every lane looks up the block
@@ -545,8 +557,10 @@ struct BlockIds {
 // a whole sequence (single pass, PLAN false: one unit per workgroup), or a
 // partition of the split-K plan (PLAN true: the workgroup takes units in
 // snake order).  Its W waves take the unit's 16-token steps round-robin.
-template <int DT, int D, int W, int GW, bool BIG_BLOCKS, bool NT, bool PLAN>
+template <int DT, int D, int W, int GW, int LAYOUT, bool NT, bool PLAN>
 __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
+  constexpr bool BIG_BLOCKS = LAYOUT != kSmallPages;
+  constexpr bool CONTIG = LAYOUT == kContiguous;
   constexpr int EB = Elem<DT>::bytes;
   constexpr int ROWB = D * EB;           // bytes per token row of one head
   constexpr int LPR = ROWB / 16;         // lanes per row
@@ -589,10 +603,11 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
       for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
     }
 
-    const int bs_mask = (1 << a.bs_log2) - 1;
-    const size_t tile_bytes = (size_t)ROWB << a.bs_log2;          // one (block, head) tile
+    // One (block, head) tile; in a contiguous cache, a sequence's rows of one head.
+    const int bs_mask = CONTIG ? -1 : (1 << a.bs_log2) - 1;
+    const size_t tile_bytes = CONTIG ? (size_t)ROWB * a.max_len : (size_t)ROWB << a.bs_log2;
     const size_t block_bytes = tile_bytes * a.num_kv_heads;
-    const int32_t* trow = a.tables + (size_t)s * a.max_blocks;
+    const int32_t* trow = CONTIG ? nullptr : a.tables + (size_t)s * a.max_blocks;
     bool bad_block = false;
 
     // Iteration k of this wave handles the 16-token step starting at step_t0(k).
@@ -602,7 +617,9 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
     // Fetch the block ids of step k into ids.nxt.
     auto fetch_ids = [&](int k) {
       const int t0 = step_t0(k);
-      if constexpr (BIG_BLOCKS) {
+      if constexpr (CONTIG) {
+        ids.nxt[0] = s;
+      } else if constexpr (BIG_BLOCKS) {
         ids.nxt[0] = trow[t0 >> a.bs_log2];
       } else {
 #pragma unroll
@@ -963,9 +980,11 @@ __device__ __forceinline__ int swz_pos(int c, int r) {
 #ifndef PA_MFMA_WPE
 #define PA_MFMA_WPE 2
 #endif
-template <int DT, int D, int W, bool BIG_BLOCKS, bool NT>
+template <int DT, int D, int W, int LAYOUT, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WPE)))
 void k_decode_mfma(const KArgs a) {
+  constexpr bool BIG_BLOCKS = LAYOUT != kSmallPages;
+  constexpr bool CONTIG = LAYOUT == kContiguous;
   constexpr int EB = 2;
   constexpr int ROWB = D * EB;
   constexpr int LPR = ROWB / 16;      // lanes (16-byte chunks) per row
@@ -1022,7 +1041,7 @@ void k_decode_mfma(const KArgs a) {
         mrec = a.minfo[ur.first + st_mi];          // in flight with the first table lookup
       }
     }
-    struct StepAt { int t0, t_end, mi; const_i32_ptr trow; };
+    struct StepAt { int t0, t_end, mi, seq; const_i32_ptr trow; };
     // The stream of a step: stream 0 while the step is within it, else the
     // highest lane whose first step is not after it (streams without steps
     // share the next stream's first step).
@@ -1033,7 +1052,7 @@ void k_decode_mfma(const KArgs a) {
         r.t0 = ur.tb + (j << 4);
         r.t_end = ur.te;
         r.mi = -1;
-        r.trow = (const_i32_ptr)(a.tables + (size_t)ts * a.max_blocks);
+        r.seq = ts;
       } else {
         const uint64_t le = __builtin_amdgcn_ballot_w64(st_first <= j);
         const int si = 63 - __builtin_clzll(le);
@@ -1041,9 +1060,9 @@ void k_decode_mfma(const KArgs a) {
                ((j - __builtin_amdgcn_readlane(st_first, si)) << 4);
         r.t_end = __builtin_amdgcn_readlane(st_te, si);
         r.mi = __builtin_amdgcn_readlane(st_mi, si);
-        r.trow = (const_i32_ptr)(a.tables +
-                                 (size_t)__builtin_amdgcn_readlane(st_seq, si) * a.max_blocks);
+        r.seq = __builtin_amdgcn_readlane(st_seq, si);
       }
+      if constexpr (!CONTIG) r.trow = (const_i32_ptr)(a.tables + (size_t)r.seq * a.max_blocks);
       return r;
     };
     // Row of the step this lane loads with instruction j (clamped to the last
@@ -1053,7 +1072,9 @@ void k_decode_mfma(const KArgs a) {
     BlockIds<BIG_BLOCKS, NDMA> ids;
     auto fetch_ids = [&](int k) {
       const StepAt st = step_at(k);
-      if constexpr (BIG_BLOCKS) {
+      if constexpr (CONTIG) {
+        ids.nxt[0] = st.seq;
+      } else if constexpr (BIG_BLOCKS) {
         ids.nxt[0] = st.trow[st.t0 >> a.bs_log2];
       } else {
 #pragma unroll
@@ -1096,8 +1117,8 @@ void k_decode_mfma(const KArgs a) {
     for (int t = 0; t < NTILE; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = kEmptyMax, lsum = 0.f;
 
-    const int bs_mask = (1 << a.bs_log2) - 1;
-    const size_t tile_bytes = (size_t)ROWB << a.bs_log2;
+    const int bs_mask = CONTIG ? -1 : (1 << a.bs_log2) - 1;
+    const size_t tile_bytes = CONTIG ? (size_t)ROWB * a.max_len : (size_t)ROWB << a.bs_log2;
     const size_t block_bytes = tile_bytes * a.num_kv_heads;
     bool bad_block = false;
 
@@ -1451,7 +1472,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       const int cnt = gfill[i];
       const int lp = glp[i];
       const bool ok = cnt <= pa.max_group_size && lp >= 0 &&
-                      lp <= (a.max_blocks << a.bs_log2) &&
+                      lp <= a.max_len &&
                       (lp & ((1 << a.bs_log2) - 1)) == 0 && (lp + P - 1) / P <= a.max_parts;
       glp[i] = ok ? lp : -1;
       gabs[i] = 0;
@@ -1856,61 +1877,71 @@ hipError_t launch1(void (*kernel)(A), dim3 grid, dim3 block, size_t lds, hipStre
 constexpr size_t kOneWorkgroupPerCuLds = 81 * 1024;
 
 template <int DT, int D, int W, int GW, bool PLAN>
-hipError_t launch_decode_t(const KArgs& ka, bool big, bool nt, int grid, hipStream_t st) {
+hipError_t launch_decode_t(const KArgs& ka, int layout, bool nt, int grid, hipStream_t st) {
   const dim3 gd(grid), bd(W * 64);
   // Split-K partitions of 512 tokens or more run one 8-wave workgroup per CU
   // (measured faster than two on the long-context batch): the unused dynamic
   // LDS below is over half of a CU's 160 KiB, so a second one does not fit.
   const size_t lds = (W == 8 && PLAN) ? kOneWorkgroupPerCuLds : 0;
-  if (big && nt) return launch1(k_decode<DT, D, W, GW, true, true, PLAN>, gd, bd, lds, st, ka);
-  if (big) return launch1(k_decode<DT, D, W, GW, true, false, PLAN>, gd, bd, lds, st, ka);
-  if (nt) return launch1(k_decode<DT, D, W, GW, false, true, PLAN>, gd, bd, lds, st, ka);
-  return launch1(k_decode<DT, D, W, GW, false, false, PLAN>, gd, bd, lds, st, ka);
+  // A contiguous cache holds no shared rows: streaming loads only.
+  if (layout == kContiguous)
+    return launch1(k_decode<DT, D, W, GW, kContiguous, true, PLAN>, gd, bd, lds, st, ka);
+  if (layout == kBigPages) {
+    if (nt) return launch1(k_decode<DT, D, W, GW, kBigPages, true, PLAN>, gd, bd, lds, st, ka);
+    return launch1(k_decode<DT, D, W, GW, kBigPages, false, PLAN>, gd, bd, lds, st, ka);
+  }
+  if (nt) return launch1(k_decode<DT, D, W, GW, kSmallPages, true, PLAN>, gd, bd, lds, st, ka);
+  return launch1(k_decode<DT, D, W, GW, kSmallPages, false, PLAN>, gd, bd, lds, st, ka);
 }
 
 // Waves per workgroup: a single pass uses 16 for one query head per wave
 // and rows of at most 256 bytes (the two register buffers then fit in 128
 // VGPRs), else 8; split-K uses 8 for partitions of 512 tokens or more, else 4.
 template <int DT, int D>
-hipError_t dispatch_gw(const KArgs& ka, int gw, int waves, bool big, bool nt, int grid,
+hipError_t dispatch_gw(const KArgs& ka, int gw, int waves, int layout, bool nt, int grid,
                        hipStream_t st) {
   if (ka.urecs == nullptr) {
     switch (gw) {
       case 1:
         if constexpr (D * Elem<DT>::bytes <= 256)
-          if (waves >= 16) return launch_decode_t<DT, D, 16, 1, false>(ka, big, nt, grid, st);
-        return launch_decode_t<DT, D, 8, 1, false>(ka, big, nt, grid, st);
-      case 2: return launch_decode_t<DT, D, 8, 2, false>(ka, big, nt, grid, st);
-      default: return launch_decode_t<DT, D, 8, 4, false>(ka, big, nt, grid, st);
+          if (waves >= 16) return launch_decode_t<DT, D, 16, 1, false>(ka, layout, nt, grid, st);
+        return launch_decode_t<DT, D, 8, 1, false>(ka, layout, nt, grid, st);
+      case 2: return launch_decode_t<DT, D, 8, 2, false>(ka, layout, nt, grid, st);
+      default: return launch_decode_t<DT, D, 8, 4, false>(ka, layout, nt, grid, st);
     }
   }
   switch (gw) {
     case 1:
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 1, true>(ka, big, nt, grid, st);
-      return launch_decode_t<DT, D, 4, 1, true>(ka, big, nt, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 1, true>(ka, layout, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 1, true>(ka, layout, nt, grid, st);
     case 2:
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 2, true>(ka, big, nt, grid, st);
-      return launch_decode_t<DT, D, 4, 2, true>(ka, big, nt, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 2, true>(ka, layout, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 2, true>(ka, layout, nt, grid, st);
     default:
-      if (waves >= 8) return launch_decode_t<DT, D, 8, 4, true>(ka, big, nt, grid, st);
-      return launch_decode_t<DT, D, 4, 4, true>(ka, big, nt, grid, st);
+      if (waves >= 8) return launch_decode_t<DT, D, 8, 4, true>(ka, layout, nt, grid, st);
+      return launch_decode_t<DT, D, 4, 4, true>(ka, layout, nt, grid, st);
   }
 }
 
 template <int DT>
-hipError_t dispatch_d(const KArgs& ka, int d, int gw, int waves, bool big, bool nt, int grid,
+hipError_t dispatch_d(const KArgs& ka, int d, int gw, int waves, int layout, bool nt, int grid,
                       hipStream_t st) {
-  return d == 64 ? dispatch_gw<DT, 64>(ka, gw, waves, big, nt, grid, st)
-                 : dispatch_gw<DT, 128>(ka, gw, waves, big, nt, grid, st);
+  return d == 64 ? dispatch_gw<DT, 64>(ka, gw, waves, layout, nt, grid, st)
+                 : dispatch_gw<DT, 128>(ka, gw, waves, layout, nt, grid, st);
 }
 
 template <int DT, int D, int W>
-hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t lds, hipStream_t st) {
+hipError_t launch_mfma_t(const KArgs& ka, int layout, bool nt, int grid, size_t lds,
+                         hipStream_t st) {
   const dim3 gd(grid), bd(W * 64);
-  if (big && nt) return launch1(k_decode_mfma<DT, D, W, true, true>, gd, bd, lds, st, ka);
-  if (big) return launch1(k_decode_mfma<DT, D, W, true, false>, gd, bd, lds, st, ka);
-  if (nt) return launch1(k_decode_mfma<DT, D, W, false, true>, gd, bd, lds, st, ka);
-  return launch1(k_decode_mfma<DT, D, W, false, false>, gd, bd, lds, st, ka);
+  if (layout == kContiguous)
+    return launch1(k_decode_mfma<DT, D, W, kContiguous, true>, gd, bd, lds, st, ka);
+  if (layout == kBigPages) {
+    if (nt) return launch1(k_decode_mfma<DT, D, W, kBigPages, true>, gd, bd, lds, st, ka);
+    return launch1(k_decode_mfma<DT, D, W, kBigPages, false>, gd, bd, lds, st, ka);
+  }
+  if (nt) return launch1(k_decode_mfma<DT, D, W, kSmallPages, true>, gd, bd, lds, st, ka);
+  return launch1(k_decode_mfma<DT, D, W, kSmallPages, false>, gd, bd, lds, st, ka);
 }
 
 // Waves per workgroup of the vector kernel for partitions of 512 tokens or
@@ -1947,13 +1978,13 @@ hipError_t launch_mfma_t(const KArgs& ka, bool big, bool nt, int grid, size_t ld
 #endif
 
 template <int DT>
-hipError_t dispatch_mfma(const KArgs& ka, int d, bool big, bool nt, int grid, hipStream_t st) {
+hipError_t dispatch_mfma(const KArgs& ka, int d, int layout, bool nt, int grid, hipStream_t st) {
   constexpr int W = PA_MFMA_WAVES;
   // Two slots of one 16-token K tile and V tile per wave; the merge of the
   // waves after the loop reuses them.
   const size_t lds = (size_t)W * 2 * 2 * 16 * d * 2;
-  if (d == 64) return launch_mfma_t<DT, 64, W>(ka, big, nt, grid, lds, st);
-  return launch_mfma_t<DT, 128, W>(ka, big, nt, grid, lds, st);
+  if (d == 64) return launch_mfma_t<DT, 64, W>(ka, layout, nt, grid, lds, st);
+  return launch_mfma_t<DT, 128, W>(ka, layout, nt, grid, lds, st);
 }
 
 template <int DT>
@@ -1991,9 +2022,13 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.num_seqs = p.num_seqs;
   ka.num_heads = p.num_heads;
   ka.num_kv_heads = p.num_kv_heads;
-  ka.bs_log2 = ilog2(p.block_size);
+  const bool contiguous = p.block_tables == nullptr;
+  // A contiguous cache is described to the kernels as one block of max_len
+  // rows per sequence, block s for sequence s.
+  ka.bs_log2 = contiguous ? 0 : ilog2(p.block_size);
   ka.max_blocks = p.max_blocks_per_seq;
-  ka.num_blocks = p.num_blocks;
+  ka.num_blocks = contiguous ? p.num_seqs : p.num_blocks;
+  ka.max_len = contiguous ? p.max_len : p.max_blocks_per_seq * p.block_size;
   ka.group = p.num_heads / p.num_kv_heads;
   // Grouped heads in 16-bit types run on the matrix cores (chunks of up to 16
   // query columns per workgroup); fp32, single heads, or the VALU-only flag
@@ -2012,7 +2047,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.scale_log2 = p.scale * kLog2e;
   // Streaming (non-temporal) K/V loads unless blocks are shared.
   const bool nt = !(p.flags & kFlagSharedKV);
-  const bool big = p.block_size >= 16;
+  const int layout = contiguous ? kContiguous : p.block_size >= 16 ? kBigPages : kSmallPages;
   // A single pass gives each workgroup a whole sequence: many waves shorten
   // its critical path and let the dispatcher balance ragged lengths.  A
   // partition of P tokens has P/16 steps; keep at least four per wave.
@@ -2039,7 +2074,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   // (block, KV head) within PA_XCD_GROUP_BYTES, c dividing the workgroups of
   // a unit and 8c dividing the grid (so the renumbering is a bijection).
   {
-    const long long tile = (long long)p.head_dim * (p.dtype == kF32 ? 4 : 2) * p.block_size;
+    const long long tile = (long long)p.head_dim * (p.dtype == kF32 ? 4 : 2) *
+                           (contiguous ? p.max_len : p.block_size);
     const int H = ka.chunks * p.num_kv_heads;
     int c = 1;
     while (2LL * c * tile <= PA_XCD_GROUP_BYTES && H % (2 * c) == 0 && grid % (16LL * c) == 0)
@@ -2064,13 +2100,13 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (mfma) {
-    e = p.dtype == kF16 ? dispatch_mfma<kF16>(ka, p.head_dim, big, nt, (int)grid, stream)
-                        : dispatch_mfma<kBF16>(ka, p.head_dim, big, nt, (int)grid, stream);
+    e = p.dtype == kF16 ? dispatch_mfma<kF16>(ka, p.head_dim, layout, nt, (int)grid, stream)
+                        : dispatch_mfma<kBF16>(ka, p.head_dim, layout, nt, (int)grid, stream);
   } else {
     switch (p.dtype) {
-      case kF32: e = dispatch_d<kF32>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;
-      case kF16: e = dispatch_d<kF16>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;
-      default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, waves, big, nt, (int)grid, stream); break;
+      case kF32: e = dispatch_d<kF32>(ka, p.head_dim, gw, waves, layout, nt, (int)grid, stream); break;
+      case kF16: e = dispatch_d<kF16>(ka, p.head_dim, gw, waves, layout, nt, (int)grid, stream); break;
+      default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, waves, layout, nt, (int)grid, stream); break;
     }
   }
   if (e != hipSuccess || ws == nullptr) return e;

@@ -19,7 +19,7 @@ struct DecodeParams {
   const void* q;
   const void* k_pool;
   const void* v_pool;
-  const int32_t* block_tables;
+  const int32_t* block_tables;  // nullptr: a contiguous cache of max_len rows per sequence
   const int32_t* context_lens;
   float* workspace;        // split-K partials; nullptr for a single pass
   int num_seqs;
@@ -34,6 +34,7 @@ struct DecodeParams {
   int partition_size;      // tokens per partition (multiple of 16)
   int max_partitions;      // partitions per sequence covered by the grid
   int flags;               // PA_FLAG_* bits
+  int max_len;             // contiguous cache: rows per (sequence, KV head); 0 when paged
   // Shared-prompt decode (seq_group == nullptr otherwise).
   const int32_t* seq_group;     // [num_seqs] group of each sequence or -1
   const int32_t* group_prefix;  // [num_groups] shared prompt tokens of each group

@@ -229,17 +229,65 @@ def make_case(w: Workload, seed: Optional[int] = None, poison: bool = True,
                 shared_groups=groups_arr, prompt_blocks=pb)
 
 
+def contiguous_cache(case: Case, max_len: Optional[int] = None, poison: bool = True,
+                     device=None):
+    """The case's K and V laid out as a contiguous cache instead of a pool:
+    [B][Hkv][max_len][d] each, row t of sequence s's region holding its
+    logical token t (the generator's own draws, kept by ``make_case(...,
+    keep_logical=True)``).  Rows past a sequence's length hold NaN (zero
+    without ``poison``).  ``max_len`` defaults to the longest length.
+
+    Host arrays in the storage dtype (uint16 bits for bf16); with ``device``,
+    torch tensors built there sequence by sequence (no host copy of the
+    whole cache)."""
+    if case.logical_k is None:
+        raise ValueError("contiguous_cache needs make_case(..., keep_logical=True)")
+    w = case.workload
+    lens = case.context_lens.astype(np.int64)
+    if max_len is None:
+        max_len = max(1, int(lens.max()))
+    if int(lens.max()) > max_len:
+        raise ValueError(f"a sequence of {int(lens.max())} tokens does not fit max_len {max_len}")
+    st = STORAGE[w.dtype]
+    fill = NAN_BITS[w.dtype] if poison else st(0)
+    shape = (w.num_seqs, w.num_kv_heads, max_len, w.head_dim)
+    if device is None:
+        kc = np.full(shape, fill, dtype=st)
+        vc = np.full(shape, fill, dtype=st)
+    else:
+        import torch
+        # bf16 travels as its int16 bit pattern and is reinterpreted at the end.
+        bits = {"f32": (np.float32, torch.float32), "f16": (np.float16, torch.float16),
+                "bf16": (np.int16, torch.int16)}[w.dtype]
+        fill_t = np.array([fill], dtype=st).view(bits[0])[0].item()
+        kc = torch.full(shape, fill_t, dtype=bits[1], device=device)
+        vc = torch.full(shape, fill_t, dtype=bits[1], device=device)
+    for s in range(w.num_seqs):
+        L = int(lens[s])
+        if not L:
+            continue
+        for cache, rows in ((kc, case.logical_k[s]), (vc, case.logical_v[s])):
+            region = np.ascontiguousarray(rows.transpose(1, 0, 2))
+            if device is None:
+                cache[s, :, :L] = region
+            else:
+                cache[s, :, :L].copy_(torch.from_numpy(region.view(bits[0])))
+    if device is not None and w.dtype == "bf16":
+        kc, vc = kc.view(torch.bfloat16), vc.view(torch.bfloat16)
+    return kc, vc
+
+
 def kv_token_count(case: Case) -> int:
     """Logical KV tokens attended by one decode step (all heads of a token
     count once)."""
     return int(case.context_lens.astype(np.int64).sum())
 
 
-def algorithmic_bytes(case: Case, unique: bool = False) -> int:
+def algorithmic_bytes(case: Case, unique: bool = False, tables: bool = True) -> int:
     """Bytes a paged decode step must move: K and V over valid rows, Q in,
     output out, block-table entries in use and lengths.  With ``unique``, a
     shared prompt's rows are counted once per group instead of once per
-    sequence."""
+    sequence; without ``tables``, no table entries (a contiguous cache)."""
     w = case.workload
     e = w.elem_bytes
     lens = case.context_lens.astype(np.int64)
@@ -248,6 +296,6 @@ def algorithmic_bytes(case: Case, unique: bool = False) -> int:
         tokens -= (w.group_size - 1) * w.groups * w.prompt_len
     kv = tokens * 2 * w.num_kv_heads * w.head_dim * e
     qo = 2 * w.num_seqs * w.num_heads * w.head_dim * e
-    nb = int(sum(ceil_div(int(L), w.block_size) for L in lens))
+    nb = int(sum(ceil_div(int(L), w.block_size) for L in lens)) if tables else 0
     meta = 4 * (nb + w.num_seqs)
     return kv + qo + meta

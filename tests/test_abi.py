@@ -113,6 +113,35 @@ def test_splitk_workspace_sizing_and_rejects(lib):
     assert call(flags=4, wsb=small) == 2
 
 
+def test_contiguous_rejects(lib):
+    """pa_decode_contiguous checks its arguments before launching anything."""
+    need = pa.pa_decode_splitk_workspace_bytes(4, 8, 128, 1000, 256)
+
+    def call(B=4, Hq=8, Hkv=2, d=128, max_len=1000, dtype=1, P_=0, ws=None, wsb=0, flags=0,
+             out=P, k=P, ln=P):
+        return lib.pa_decode_contiguous(out, P, k, P, ln, B, Hq, Hkv, d, max_len, 0.088, dtype,
+                                        P_, ws, wsb, flags, None)
+
+    assert call(max_len=0) == 2
+    assert call(max_len=-5) == 2
+    assert call(d=96) == 3
+    assert call(dtype=9) == 3
+    assert call(Hq=6, Hkv=4) == 2
+    assert call(flags=1) == 2                  # no shared rows in a contiguous cache
+    assert call(flags=4) == 2
+    assert call(out=0) == 1
+    assert call(ln=0) == 1
+    assert call(k=P + 4) == 2
+    assert call(max_len=1 << 30) in (2, 3)     # rows of one head past 2 GiB
+    assert call(max_len=(1 << 23) + 1) == 3    # 2 GiB + 256 bytes per (sequence, head)
+    assert call(P_=24) == 2
+    assert call(P_=-16) == 2
+    assert call(P_=256) == 4                   # split-K needs the workspace
+    assert call(P_=256, ws=P, wsb=need - 1) == 4
+    assert call(P_=256, ws=P + 4, wsb=need) == 2
+    assert call(B=0, out=0, k=0, ln=0) == 0    # nothing to do
+
+
 def test_noalloc_rejects_before_touching_the_device(lib):
     """pa_decode_splitk_noalloc checks its arguments like pa_decode_splitk
     and refuses sizes whose workspace exceeds the static scratch, all before

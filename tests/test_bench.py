@@ -24,9 +24,23 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stdout
 
 
+@pytest.mark.parametrize("args", [("--through-table",),
+                                  ("--contiguous", "--through-table", "--workload", "tiny"),
+                                  ("--contiguous", "--one-block"),
+                                  ("--contiguous", "--workload", "shared_prefix")])
+def test_layout_options_that_do_not_combine_are_refused(args):
+    """Refused before any input is generated or the GPU is touched."""
+    r = _bench(*args)
+    assert r.returncode == 1
+    assert "needs" in r.stderr or "runs the single-pass" in r.stderr, r.stderr
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("args", [("--workload", "tiny"),
-                                  ("--workload", "tiny", "--entry", "splitk", "--partition", "16")])
+                                  ("--workload", "tiny", "--entry", "splitk", "--partition", "16"),
+                                  ("--workload", "tiny", "--contiguous"),
+                                  ("--workload", "tiny", "--contiguous", "--entry", "splitk",
+                                   "--partition", "16")])
 def test_bench_prints_one_json_line(args):
     r = _bench(*args, "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
     assert r.returncode == 0, r.stderr[-2000:]

@@ -1,0 +1,153 @@
+"""GPU tests of decode over a contiguous KV cache (pa_decode_contiguous).
+
+The contiguous cache is the layout paging replaces: every sequence owns
+max_len rows per KV head ("IO-5 vLLM Paged Attention", section 1).  Paging
+must not change the attention ("IO-5 vLLM Paged Attention", "5 common
+misconceptions"), so the kernel is checked two ways:
+
+* against the fp64 oracle's attention over the generator's logical rows,
+  within the max-abs bounds 1e-5 (fp32), 2e-3 (fp16), 1e-2 (bf16);
+* bit for bit against the paged entries on a pool holding the same rows:
+  the kernels are the same with the table lookup removed, so any difference
+  is an indexing mistake.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_438_amd as pa
+from synthetic import GQA70B, LLAMA7B, WORKLOADS, Workload, contiguous_cache, make_case, small_variant
+from tests.gpu_util import TOL, DevCase, dev_array, host_bits, host_f64, note
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [small_variant(w) for w in WORKLOADS.values()]
+ENTRIES = [("single", 0), ("splitk", 16), ("splitk", 64), ("splitk", 512)]
+
+
+def _contig_oracle(c):
+    return oracle.contiguous_attention(c.q, c.logical_k, c.logical_v, c.scale, c.dtype,
+                                       c.workload.num_kv_heads)
+
+
+def _check_close(got, ref, dtype, what):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    note(f"  {what}: max|err| = {err:.3e} (bound {TOL[dtype]:.0e})")
+    assert err <= TOL[dtype], f"{what}: max abs error {err} > {TOL[dtype]}"
+
+
+def _run(d, kc, vc, P, valu_only=False):
+    return pa.pa_decode_contiguous(d.q, kc, vc, d.lens, scale=float(d.c.scale), partition_size=P,
+                                   valu_only=valu_only)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_contiguous_parity_and_bitwise_equal_to_paged(w):
+    c = make_case(w, keep_logical=True)
+    ref = _contig_oracle(c)
+    d = DevCase(c)
+    # Region length: the longest sequence, and 37 rows more (a stride that is
+    # not a multiple of 16 rows).
+    for extra in (0, 37):
+        max_len = int(c.context_lens.max()) + extra
+        kc, vc = contiguous_cache(c, max_len, device="cuda")
+        for entry, P in ENTRIES:
+            for valu in ((False, True) if w.num_heads > w.num_kv_heads else (False,)):
+                what = f"{w.name}/max_len={max_len}/{entry}/{P}/valu={valu}"
+                note(f"contiguous: {what} seed={c.seed} lens={c.context_lens.tolist()}")
+                got = _run(d, kc, vc, P, valu_only=valu)
+                paged = d.decode(entry, P or None, valu_only=valu)
+                torch.cuda.synchronize()
+                _check_close(host_f64(got), ref, w.dtype, what)
+                assert host_bits(got).tobytes() == host_bits(paged).tobytes(), what
+
+
+def edge_workload(name, lens, Hq, Hkv, d, dtype, seed=23):
+    return Workload(name=name, num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                    block_size=16, dtype=dtype, seed=seed, length_kind="fixed",
+                    lengths=tuple(lens), max_blocks_per_seq=max(1, -(-max(lens) // 16)) + 1)
+
+
+EDGE = [
+    # max_len = the longest length, which is not a multiple of 16
+    ("mha_f16", (0, 1, 15, 16, 17, 63, 64, 65, 100), 2, 2, 128, "f16", 0),
+    ("gqa_bf16_g8", (1, 2, 16, 33, 99, 100, 0), 16, 2, 128, "bf16", 0),
+    ("gqa_f16_g4_d64", (0, 5, 48, 49, 211), 8, 2, 64, "f16", 0),
+    ("f32_g2", (3, 31, 32, 33, 77), 4, 2, 64, "f32", 0),
+    # one row per sequence
+    ("max_len_1", (1, 0, 1, 1), 4, 4, 128, "bf16", 0),
+    # longest sequence far below the region length
+    ("slack", (5, 17, 40), 8, 1, 128, "bf16", 3000),
+]
+
+
+@pytest.mark.parametrize("spec", EDGE, ids=lambda s: s[0])
+def test_contiguous_edge_lengths(spec):
+    name, lens, Hq, Hkv, dd, dtype, slack = spec
+    w = edge_workload(name, lens, Hq, Hkv, dd, dtype)
+    c = make_case(w, keep_logical=True)
+    ref = _contig_oracle(c)
+    d = DevCase(c)
+    max_len = max(lens) + slack
+    kc, vc = contiguous_cache(c, max_len, device="cuda")
+    for P in (0, 16, 48, 512):
+        note(f"contiguous edge: {name} max_len={max_len} P={P} lens={list(lens)}")
+        got = _run(d, kc, vc, P)
+        paged = d.decode("single" if P == 0 else "splitk", P or None)
+        torch.cuda.synchronize()
+        g = host_f64(got)
+        _check_close(g, ref, dtype, f"{name}/P={P}")
+        assert host_bits(got).tobytes() == host_bits(paged).tobytes()
+        for s, L in enumerate(lens):
+            if L == 0:
+                assert np.all(g[s] == 0.0), "empty sequence must give zeros"
+
+
+def test_contiguous_lengths_outside_the_region_give_nan():
+    """A length below 0 or above max_len breaks the device contract: that
+    sequence's rows are NaN, the others are unaffected, and nothing is read
+    outside the cache."""
+    w = edge_workload("violations", (10, 40, 64, 7), 8, 2, 128, "bf16")
+    c = make_case(w, keep_logical=True)
+    ref = _contig_oracle(c)
+    d = DevCase(c)
+    max_len = 64
+    kc, vc = contiguous_cache(c, max_len, device="cuda")
+    lens = c.context_lens.copy()
+    lens[0] = max_len + 1
+    lens[3] = -1
+    dl = dev_array(lens)
+    for P in (0, 16):
+        note(f"contiguous violations: P={P} lens={lens.tolist()}")
+        out = pa.pa_decode_contiguous(d.q, kc, vc, dl, scale=float(c.scale), partition_size=P)
+        torch.cuda.synchronize()
+        g = host_f64(out)
+        assert np.all(np.isnan(g[0])) and np.all(np.isnan(g[3]))
+        _check_close(g[1:3], ref[1:3], "bf16", f"violations/P={P}")
+
+
+@pytest.mark.parametrize("w,P", [(LLAMA7B, 0), (GQA70B, 8192)], ids=["llama2_7b", "gqa_70b"])
+def test_contiguous_full_size_bitwise_equal_to_paged(w, P):
+    """The page-size comparison's workloads at full size: every output bit
+    equals the paged call's, and a sample of rows meets the oracle bound."""
+    c = make_case(w, keep_logical=True)
+    d = DevCase(c)
+    max_len = int(c.context_lens.max())
+    note(f"contiguous full size: {w.name} P={P} max_len={max_len}")
+    kc, vc = contiguous_cache(c, max_len, device="cuda")
+    got = _run(d, kc, vc, P)
+    paged = d.decode("single" if P == 0 else "splitk", P or None)
+    torch.cuda.synchronize()
+    assert host_bits(got).tobytes() == host_bits(paged).tobytes()
+    g = host_f64(got)
+    rng = np.random.default_rng(5)
+    for s in sorted(rng.choice(w.num_seqs, 6, replace=False).tolist()) + [int(np.argmax(c.context_lens))]:
+        r = oracle.contiguous_attention(c.q[s:s + 1], [c.logical_k[s]], [c.logical_v[s]], c.scale,
+                                        c.dtype, w.num_kv_heads)
+        _check_close(g[s:s + 1], r, w.dtype, f"{w.name}/seq {s}")
+    del kc, vc
+    torch.cuda.empty_cache()

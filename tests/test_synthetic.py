@@ -4,7 +4,8 @@ import pytest
 import torch
 
 from synthetic import (GQA70B, LLAMA7B, LONG_BS512, SHARED_PREFIX, TINY, WORKLOADS,
-                       algorithmic_bytes, ceil_div, f32_to_bf16_bits, make_case, small_variant)
+                       algorithmic_bytes, ceil_div, contiguous_cache, f32_to_bf16_bits, make_case,
+                       small_variant)
 
 SMALL = [small_variant(w) for w in WORKLOADS.values()]
 
@@ -53,6 +54,42 @@ def test_structure(w):
             assert np.all(kb == 0x7FC0)
         else:
             assert np.all(np.isnan(kb))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_contiguous_cache_layout(w):
+    """Row t of KV head g in sequence s's region is the same bytes as the pool
+    row the table names for it; rows past the length are NaN."""
+    c = make_case(w, keep_logical=True)
+    extra = 5
+    max_len = int(c.context_lens.max()) + extra
+    kc, vc = contiguous_cache(c, max_len)
+    assert kc.shape == (w.num_seqs, w.num_kv_heads, max_len, w.head_dim) == vc.shape
+    assert kc.dtype == c.k_pool.dtype
+    bs = w.block_size
+    for s in range(w.num_seqs):
+        L = int(c.context_lens[s])
+        for t in range(L):
+            blk, r = c.block_tables[s, t // bs], t % bs
+            assert kc[s, :, t].tobytes() == c.k_pool[blk, :, r].tobytes()
+            assert vc[s, :, t].tobytes() == c.v_pool[blk, :, r].tobytes()
+        tail = kc[s, :, L:]
+        assert np.all(tail == 0x7FC0) if w.dtype == "bf16" else np.all(np.isnan(tail))
+    with pytest.raises(ValueError):
+        contiguous_cache(c, int(c.context_lens.max()) - 1)
+    with pytest.raises(ValueError):
+        contiguous_cache(make_case(w), max_len)          # logical rows not kept
+
+
+def test_contiguous_cache_on_a_torch_device_matches_host():
+    """The device builder (here on the CPU device) lays out the same bits."""
+    for w in (small_variant(GQA70B), small_variant(LLAMA7B)):
+        c = make_case(w, keep_logical=True)
+        kc, vc = contiguous_cache(c, int(c.context_lens.max()) + 3)
+        kt, vt = contiguous_cache(c, int(c.context_lens.max()) + 3, device="cpu")
+        for host, dev in ((kc, kt), (vc, vt)):
+            bits = dev.view(torch.int16).numpy() if dev.dtype == torch.bfloat16 else dev.numpy()
+            assert bits.tobytes() == host.tobytes()
 
 
 def test_lengths_follow_workloads():
