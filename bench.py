@@ -323,6 +323,9 @@ def main() -> int:
                     help="with --contiguous: the paged entry over the same contiguous memory, "
                          "seen as one block per sequence through an identity table (isolates "
                          "the cost of the table lookups)")
+    ap.add_argument("--shuffled", action="store_true",
+                    help="with --through-table: the sequences' regions moved to shuffled "
+                         "slots of the same memory, the table naming each one's slot")
     ap.add_argument("--one-block", action="store_true",
                     help="paged decode with one block per sequence, as long as the longest "
                          "possible sequence")
@@ -378,6 +381,8 @@ def main() -> int:
                                    longest <= 65536):
         raise SystemExit("--through-table needs --contiguous and a longest context that is a "
                          "power of two of at most 65536 (a valid block size)")
+    if args.shuffled and not args.through_table:
+        raise SystemExit("--shuffled needs --through-table")
     if args.one_block or args.block_size:
         bs = args.block_size or 1 << (longest - 1).bit_length()
         if args.one_block and bs < longest:
@@ -423,8 +428,16 @@ def main() -> int:
         kc, vc = contiguous_cache(case, longest, device=dev)
         case.logical_k = case.logical_v = None
         # The same memory as a pool of one block per sequence, block s for
-        # sequence s.
+        # sequence s; shuffled, sequence s's region moves to slot perm[s].
         ident = torch.arange(w.num_seqs, dtype=torch.int32, device=dev).reshape(-1, 1)
+        if args.shuffled:
+            perm = torch.from_numpy(np.random.default_rng(case.seed).permutation(w.num_seqs))
+            perm = perm.to(dev)
+            kc2, vc2 = torch.empty_like(kc), torch.empty_like(vc)
+            kc2[perm], vc2[perm] = kc, vc
+            kc, vc = kc2, vc2
+            del kc2, vc2
+            ident = perm.to(torch.int32).reshape(-1, 1).contiguous()
     else:
         kp, vp = d(case.k_pool, dt), d(case.v_pool, dt)
         kn, vn = d(case.k_new, dt), d(case.v_new, dt)
@@ -574,7 +587,9 @@ def main() -> int:
                    "partition_size": P, "accumulate": "f32", "shared_kv_flag": shared,
                    "valu_only": bool(args.valu_only),
                    "global_batch": w.num_seqs, "kv_tokens": tokens,
-                   "kv_layout": ("contiguous cache through an identity table"
+                   "kv_layout": ("contiguous cache, regions shuffled, through a table"
+                                 if args.shuffled else
+                                 "contiguous cache through an identity table"
                                  if args.through_table else "contiguous cache"
                                  if args.contiguous else "paged pool"),
                    "step": "decode (contiguous cache, no paged write)" if args.contiguous
