@@ -5,9 +5,9 @@ Each case draws its own shape from a counter-seeded generator: dtype,
 head_dim, KV heads, query heads per KV head (1 to 16, including ones that do
 not divide 16), block size 1 to 256, batch, a length mix with zeros and block
 boundaries, and the entry point (single pass, split-K at one of seven
-partition sizes, the vector-ALU-only flag, or sharing-aware decode over
-random prompt groups).  The case is printed before it runs, so a failure
-names its draw.
+partition sizes, the vector-ALU-only flag, sharing-aware decode over random
+prompt groups, or decode over a contiguous cache with a random region
+length).  The case is printed before it runs, so a failure names its draw.
 """
 from __future__ import annotations
 
@@ -17,13 +17,14 @@ import torch
 
 import oracle
 import paged_kv_cache_438_amd as pa
-from synthetic import SHARED_PREFIX, TINY, make_case
-from tests.gpu_util import TOL, DevCase, dev_array, host_f64, note
+from synthetic import SHARED_PREFIX, TINY, contiguous_cache, make_case
+from tests.gpu_util import TOL, DevCase, dev_array, host_bits, host_f64, note
 
 pytestmark = pytest.mark.gpu
 
 N_PLAIN = 60
 N_SHARED = 24
+N_CONTIGUOUS = 24
 
 
 def _plain_case(i):
@@ -117,3 +118,30 @@ def test_random_shared_prefix_matches_oracle(i):
     ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
                         c.block_size, c.dtype)
     _check(got, ref, w.dtype, f"sweep shared {i}")
+
+
+@pytest.mark.parametrize("i", range(N_CONTIGUOUS))
+def test_random_contiguous_matches_oracle_and_paged(i):
+    """pa_decode_contiguous on a random shape, with a region 0 to 40 rows
+    longer than the longest sequence: within the bound of the oracle's
+    attention over the logical rows, and bit-identical to the paged entry on
+    the same rows."""
+    w, entry, P = _plain_case(1000 + i)
+    c = make_case(w, keep_logical=True)
+    extra = int(np.random.default_rng(99_000 + i).integers(0, 41))
+    max_len = max(1, int(c.context_lens.max()) + extra)
+    part = 0 if entry.startswith("single") else P
+    valu = entry.endswith("_valu")
+    note(f"sweep contiguous {i}: {w.dtype} d={w.head_dim} Hq={w.num_heads} "
+         f"Hkv={w.num_kv_heads} lens={list(w.lengths)} max_len={max_len} P={part} valu={valu}")
+    d = DevCase(c)
+    kc, vc = contiguous_cache(c, max_len, device="cuda")
+    got = pa.pa_decode_contiguous(d.q, kc, vc, d.lens, scale=float(c.scale), partition_size=part,
+                                  valu_only=valu)
+    paged = d.decode("single" if part == 0 else "splitk", partition_size=part or None,
+                     valu_only=valu)
+    torch.cuda.synchronize()
+    ref = oracle.contiguous_attention(c.q, c.logical_k, c.logical_v, c.scale, c.dtype,
+                                      w.num_kv_heads)
+    _check(host_f64(got), ref, w.dtype, f"sweep contiguous {i}")
+    assert host_bits(got).tobytes() == host_bits(paged).tobytes(), f"sweep contiguous {i}"
