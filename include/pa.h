@@ -219,9 +219,9 @@ int pa_decode_splitk_noalloc(void* out, const void* q, const void* k_pool, const
  * Bytes of device workspace pa_decode_shared_prefix needs: the split-K
  * partials for ceil(max_context_len / partition_size) + 1 partitions per
  * sequence, the launch plan (its unit records also cover every group's
- * prompt partitions), the group tables (a 16-byte member record and 8
- * bytes of plan scratch per sequence, 12 bytes per group), and a 4-byte
- * merge counter per (sequence, query head).  Returns 0 for invalid sizes.
+ * prompt partitions), and the group tables (a 16-byte member record and 8
+ * bytes of plan scratch per sequence, 12 bytes per group).  Returns 0 for
+ * invalid sizes.
  */
 size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int head_dim,
                                                int max_context_len, int partition_size,
@@ -254,9 +254,7 @@ size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int 
  * and ungrouped sequences, are cut into partitions of their own.  A member
  * whose only partition is the absorbing one gets its output written
  * directly; otherwise partials are merged in fixed order as in
- * pa_decode_splitk, but inside the partition launch: the workgroup that
- * writes the last partial of a (sequence, head) merges them (two launches
- * per call, plan and partitions).  Results are deterministic: the plan sorts each group's
+ * pa_decode_splitk.  Results are deterministic: the plan sorts each group's
  * members by sequence index.  A member's bits may depend on the lengths of
  * the members sorted before it in its chunk (which wave takes which of its
  * absorbed steps), not on their K/V values as long as those are finite.

@@ -205,11 +205,7 @@ template <> __device__ __forceinline__ void store_elem<kBF16>(void* out, size_t 
 //   tb, te token range [tb, te) of the unit's main stream
 //   first, cnt, lp, ts  (prompt units) the group's members in the member
 //          list, its prompt length, and a member whose table supplies the
-//          prompt's blocks; (a sequence's units) cnt is the sequence's
-//          number of partitions
-// A member record (int4) holds the member's sequence, its absorbed own
-// token range and, in .w, kUnit* flags plus its number of partitions in the
-// low 24 bits.
+//          prompt's blocks
 struct __attribute__((aligned(16))) URec {
   int s, pf, tb, te, first, cnt, lp, ts;
 };
@@ -252,10 +248,6 @@ struct KArgs {
   const URec* urecs;    // split-K plan: the units, longest first (nullptr: single pass)
   const int2* split;    // split-K plan: (sequence, partitions) of the sequences to merge
   const int4* minfo;    // split-K plan: members of the prompt groups
-  // Sharing-aware decode: one counter per (sequence, query head) of the
-  // sequences with several partitions (zeroed by the plan); the partition
-  // launch merges them itself.  nullptr: the reduce launch merges.
-  int* merge_cnt;
   // Sharing-aware decode, read by the plan only (nullptr otherwise): the
   // group of each sequence (-1: none) and each group's shared prompt length.
   const int32_t* seq_group;
@@ -421,7 +413,7 @@ struct UnitCursor {
 // partition slot of that sequence it fills, and whether it writes the output
 // directly (the sequence has a single partition).
 struct Col {
-  int seq, head, part, np;      // np: the sequence's partitions
+  int seq, head, part;
   bool valid, direct, bad;
 };
 // Column n of chunk ch of a unit: for a prompt unit, member cc / G of the
@@ -441,14 +433,12 @@ __device__ __forceinline__ Col column_of(const KArgs& a, const URec& r, int g, i
     c.bad = (m.w & kUnitBad) != 0;
     c.valid = c.valid && !c.bad;       // an out-of-contract member writes its NaN row itself
     c.direct = (m.w & kUnitDirect) != 0;
-    c.np = m.w & kPartMask;
   } else {
     c.valid = n < ncols;
     c.seq = r.s;
     c.head = g * a.group + cc;
     c.bad = (r.pf & kUnitBad) != 0;
     c.direct = (r.pf & kUnitDirect) != 0;
-    c.np = r.cnt;
   }
   return c;
 }
@@ -990,12 +980,7 @@ __device__ __forceinline__ int swz_pos(int c, int r) {
 #ifndef PA_MFMA_WPE
 #define PA_MFMA_WPE 2
 #endif
-template <int DT, int D>
-__device__ void merge_partitions(const KArgs& a, int item, int np, int lane);
-
-// MERGE: the launch merges split sequences itself (sharing-aware decode,
-// a.merge_cnt set); otherwise a reduce launch follows.
-template <int DT, int D, int W, int LAYOUT, bool NT, bool MERGE>
+template <int DT, int D, int W, int LAYOUT, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(PA_MFMA_WPE)))
 void k_decode_mfma(const KArgs a) {
   constexpr bool BIG_BLOCKS = LAYOUT != kSmallPages;
@@ -1292,14 +1277,12 @@ void k_decode_mfma(const KArgs a) {
     float* s_l = s_m + W * 16;                              // [W][16]
     int* s_bad = reinterpret_cast<int*>(s_l + W * 16);
     int* s_col = s_bad + 1;                                 // [16][4]: seq, head, part, flags
-    int* s_last = s_col + 64;                               // [16] (in-launch merges)
     if (threadIdx.x == 0) *s_bad = 0;
     if (threadIdx.x < 16) {
       s_col[4 * n] = col.seq;
       s_col[4 * n + 1] = col.head;
       s_col[4 * n + 2] = col.part;
-      s_col[4 * n + 3] = (col.valid ? 1 : 0) | (col.direct ? 2 : 0) | (col.bad ? 4 : 0) |
-                         (MERGE ? col.np << 3 : 0);
+      s_col[4 * n + 3] = (col.valid ? 1 : 0) | (col.direct ? 2 : 0) | (col.bad ? 4 : 0);
     }
     __syncthreads();
     if (bad_block) *s_bad = 1;
@@ -1340,43 +1323,6 @@ void k_decode_mfma(const KArgs a) {
         if (poisoned) { as = __builtin_nanf(""); ls = __builtin_nanf(""); }
         a.ws_acc[slot * D + e] = as;
         if (e == 0) a.ws_ml[slot] = make_float2(M, ls);
-      }
-    }
-    if constexpr (MERGE) {
-      // Sharing-aware decode merges in this launch: per (sequence, head) of
-      // a column that wrote a partial, a counter counts the partials written
-      // so far, and the workgroup that writes the last one merges them all.
-      // Every wave's partials reach device scope before the counter moves
-      // (release), and the merging workgroup reads the others' partials only
-      // after it has seen the count (acquire).  The merge runs in partition
-      // order, so which workgroup is last does not change any bit.
-      bool partials = false;
-      for (int c = 0; c < nh; ++c) partials |= (s_col[4 * c + 3] & 3) == 1;
-      if (partials) {                           // uniform: read from LDS by every thread
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (threadIdx.x < 16) {
-          const int cf = s_col[4 * n + 3];
-          int last = 0;
-          if (n < nh && (cf & 3) == 1) {
-            const int item = s_col[4 * n] * a.num_heads + s_col[4 * n + 1];
-            const int done = __hip_atomic_fetch_add(a.merge_cnt + item, 1, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-            last = done + 1 == (cf >> 3);
-          }
-          s_last[n] = last;
-        }
-        __syncthreads();
-        bool any = false;
-        for (int c = 0; c < nh; ++c) any |= s_last[c] != 0;
-        if (any) {
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-          for (int c = wave; c < nh; c += W)
-            if (s_last[c])
-              merge_partitions<DT, D>(a, s_col[4 * c] * a.num_heads + s_col[4 * c + 1],
-                                      s_col[4 * c + 3] >> 3, lane);
-        }
       }
     }
     __syncthreads();                            // the next unit's loads refill the slots
@@ -1554,8 +1500,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       const SeqLayout ml = layout(s);
       const bool own = ml.absorbed && !ml.bad;
       pa.minfo[lo + rank] = make_int4(s, own ? ml.lp : 0, own ? ml.len : 0,
-                                      (ml.nparts == 1 ? kUnitDirect : 0) | (ml.bad ? kUnitBad : 0) |
-                                          ml.nparts);
+                                      (ml.nparts == 1 ? kUnitDirect : 0) | (ml.bad ? kUnitBad : 0));
       if (own) atomicAdd(&gabs[gi], (ml.len - ml.lp) / (((hi - lo) * a.group + 15) / 16));
     }
     __syncthreads();
@@ -1619,15 +1564,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     for (int s = tid; s < B; s += kPlanThreads) {
       const SeqLayout lay = layout(s);
       const int own = lay.nparts - lay.np_pre;
-      if (pass == 0 && lay.nparts > 1) {
-        pa.split[atomicAdd(&s_split, 1)] = make_int2(s, lay.nparts);
-        if (a.merge_cnt != nullptr)
-          for (int h = 0; h < a.num_heads; ++h) a.merge_cnt[(size_t)s * a.num_heads + h] = 0;
-      }
+      if (pass == 0 && lay.nparts > 1) pa.split[atomicAdd(&s_split, 1)] = make_int2(s, lay.nparts);
       URec r;
       r.s = s;
-      r.first = r.lp = 0;
-      r.cnt = lay.nparts;
+      r.first = r.cnt = r.lp = 0;
       r.ts = s;
       if (lay.nparts == 0) {                     // empty or out of contract: one empty unit
         r.pf = kUnitDirect | (lay.bad ? kUnitBad : 0);
@@ -1679,79 +1619,74 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wave merges the np partitions of one (sequence, head), item =
-// sequence * num_heads + head: with M = max_p m_p,
+// One wave per (sequence, head) of the sequences the plan listed as split
+// merges their partitions: with M = max_p m_p,
 //   out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
 // Lanes first read the (m, l) pairs of 64 partitions at a time, then every
 // lane accumulates its head-dim elements over the partitions in order
 // p = 0, 1, ..., taking each weight from the lane that computed it, with
-// eight loads in flight.  All sums run in a fixed order, so the bits do not
-// depend on which wave merges or when.  The reduce launch runs it for every
-// head of every sequence the plan listed as split; sharing-aware decode runs
-// it in the partition launch (k_decode_mfma).
-template <int DT, int D>
-__device__ __forceinline__ void merge_partitions(const KArgs& a, int item, int np, int lane) {
-  constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
-  constexpr int U = 8;                 // partition loads in flight
-  const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
-  const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
-
-  float M = kEmptyMax;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
-  M = wave_max(M);
-  float lsum = 0.f;
-  for (int p = lane; p < np; p += 64) lsum += ml[p].y * fast_exp2(ml[p].x - M);
-  const float inv = 1.f / wave_sum(lsum);
-
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += 64) {
-    const float wl = p0 + lane < np ? fast_exp2(ml[p0 + lane].x - M) : 0.f;
-    const int cnt = min(64, np - p0);
-    auto add = [&](int j, const float* v) {
-      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                    __builtin_bit_cast(int, wl), j));
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, v[e], acc[e]);
-    };
-    int j = 0;
-    for (; j + U <= cnt; j += U) {
-      float v[U][EPL];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float* src = pacc + (size_t)(p0 + j + u) * D;
-        if constexpr (EPL == 2) {
-          const float2 t = *reinterpret_cast<const float2*>(src);
-          v[u][0] = t.x;
-          v[u][1] = t.y;
-        } else {
-          v[u][0] = src[0];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) add(j + u, v[u]);
-    }
-    for (; j < cnt; ++j) {
-      float v[EPL];
-      const float* src = pacc + (size_t)(p0 + j) * D;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) v[e] = src[e];
-      add(j, v);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e)
-    store_elem<DT>(a.out, (size_t)item * D + lane * EPL + e, acc[e] * inv);
-}
-
+// eight loads in flight.  All sums run in a fixed order, so reruns give
+// identical bits (the order of the list does not matter).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
+  constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
+  constexpr int U = 8;                 // partition loads in flight
   const int lane = threadIdx.x & 63;
   const int total = a.n_units[1] * a.num_heads;
   for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < total; it += gridDim.x * 4) {
     const int2 sp = a.split[it / a.num_heads];   // (sequence, partitions)
-    merge_partitions<DT, D>(a, sp.x * a.num_heads + it % a.num_heads, sp.y, lane);
+    const int item = sp.x * a.num_heads + it % a.num_heads;
+    const int np = sp.y;
+    const float2* ml = a.ws_ml + (size_t)item * a.max_parts;
+    const float* pacc = a.ws_acc + (size_t)item * a.max_parts * D + lane * EPL;
+
+    float M = kEmptyMax;
+    for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[p].x);
+    M = wave_max(M);
+    float lsum = 0.f;
+    for (int p = lane; p < np; p += 64) lsum += ml[p].y * fast_exp2(ml[p].x - M);
+    const float inv = 1.f / wave_sum(lsum);
+
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const float wl = p0 + lane < np ? fast_exp2(ml[p0 + lane].x - M) : 0.f;
+      const int cnt = min(64, np - p0);
+      auto add = [&](int j, const float* v) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int, wl), j));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+      };
+      int j = 0;
+      for (; j + U <= cnt; j += U) {
+        float v[U][EPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float* src = pacc + (size_t)(p0 + j + u) * D;
+          if constexpr (EPL == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(src);
+            v[u][0] = t.x;
+            v[u][1] = t.y;
+          } else {
+            v[u][0] = src[0];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(j + u, v[u]);
+      }
+      for (; j < cnt; ++j) {
+        float v[EPL];
+        const float* src = pacc + (size_t)(p0 + j) * D;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[e] = src[e];
+        add(j, v);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      store_elem<DT>(a.out, (size_t)item * D + lane * EPL + e, acc[e] * inv);
   }
 }
 
@@ -1995,27 +1930,18 @@ hipError_t dispatch_d(const KArgs& ka, int d, int gw, int waves, int layout, boo
                  : dispatch_gw<DT, 128>(ka, gw, waves, layout, nt, grid, st);
 }
 
-template <int DT, int D, int W, bool MERGE>
-hipError_t launch_mfma_m(const KArgs& ka, int layout, bool nt, int grid, size_t lds,
-                         hipStream_t st) {
-  const dim3 gd(grid), bd(W * 64);
-  if (layout == kBigPages) {
-    if (nt) return launch1(k_decode_mfma<DT, D, W, kBigPages, true, MERGE>, gd, bd, lds, st, ka);
-    return launch1(k_decode_mfma<DT, D, W, kBigPages, false, MERGE>, gd, bd, lds, st, ka);
-  }
-  if (nt) return launch1(k_decode_mfma<DT, D, W, kSmallPages, true, MERGE>, gd, bd, lds, st, ka);
-  return launch1(k_decode_mfma<DT, D, W, kSmallPages, false, MERGE>, gd, bd, lds, st, ka);
-}
-
 template <int DT, int D, int W>
 hipError_t launch_mfma_t(const KArgs& ka, int layout, bool nt, int grid, size_t lds,
                          hipStream_t st) {
-  // A contiguous cache holds no shared prompts: no in-launch merges.
+  const dim3 gd(grid), bd(W * 64);
   if (layout == kContiguous)
-    return launch1(k_decode_mfma<DT, D, W, kContiguous, true, false>, dim3(grid), dim3(W * 64),
-                   lds, st, ka);
-  if (ka.merge_cnt != nullptr) return launch_mfma_m<DT, D, W, true>(ka, layout, nt, grid, lds, st);
-  return launch_mfma_m<DT, D, W, false>(ka, layout, nt, grid, lds, st);
+    return launch1(k_decode_mfma<DT, D, W, kContiguous, true>, gd, bd, lds, st, ka);
+  if (layout == kBigPages) {
+    if (nt) return launch1(k_decode_mfma<DT, D, W, kBigPages, true>, gd, bd, lds, st, ka);
+    return launch1(k_decode_mfma<DT, D, W, kBigPages, false>, gd, bd, lds, st, ka);
+  }
+  if (nt) return launch1(k_decode_mfma<DT, D, W, kSmallPages, true>, gd, bd, lds, st, ka);
+  return launch1(k_decode_mfma<DT, D, W, kSmallPages, false>, gd, bd, lds, st, ka);
 }
 
 // Waves per workgroup of the vector kernel for partitions of 512 tokens or
@@ -2088,11 +2014,6 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.urecs = ws ? reinterpret_cast<const URec*>(ws + wl.units) : nullptr;
   ka.split = ws ? reinterpret_cast<const int2*>(ws + wl.split) : nullptr;
   ka.minfo = shared ? reinterpret_cast<const int4*>(ws + wl.minfo) : nullptr;
-  // Sharing-aware decode merges split sequences inside the partition launch
-  // (no reduce launch): in the shared-prompt batches it serves, most members
-  // are absorbed into their group's last prompt partition and write their
-  // rows directly, and an empty reduce launch would cost a kernel boundary.
-  ka.merge_cnt = shared ? reinterpret_cast<int*>(ws + wl.merge_cnt) : nullptr;
   // The caller's groups: read by the plan only.
   ka.seq_group = shared ? p.seq_group : nullptr;
   ka.group_prefix = shared ? p.group_prefix : nullptr;
@@ -2188,7 +2109,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
       default: e = dispatch_d<kBF16>(ka, p.head_dim, gw, waves, layout, nt, (int)grid, stream); break;
     }
   }
-  if (e != hipSuccess || ws == nullptr || ka.merge_cnt != nullptr) return e;
+  if (e != hipSuccess || ws == nullptr) return e;
   // One wave per (split sequence, head), at most PA_REDUCE_MAX_WGS
   // workgroups of four waves striding over them (the count is on the device).
   const int rgrid = std::min((p.num_seqs * p.num_heads + 3) / 4, PA_REDUCE_MAX_WGS);

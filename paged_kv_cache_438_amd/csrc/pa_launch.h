@@ -61,8 +61,7 @@ struct CacheWriteParams {
 // Byte offsets of the parts of the split-K workspace (pa_workspace.cpp).
 struct WsLayout {
   size_t max_units;   // capacity of the unit list
-  size_t ml, n_units, units, split, minfo, arrival, group_fill, group_start, group_lp, merge_cnt,
-      total;
+  size_t ml, n_units, units, split, minfo, arrival, group_fill, group_start, group_lp, total;
 };
 // Bytes of one unit record of the plan.
 constexpr size_t kUnitRecordBytes = 32;

@@ -15,9 +15,7 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 //           [(G + B) * Pmax] of 32 bytes, split list [B] of (sequence,
 //           partitions) int pairs
 //   with prompt groups: member records [B] of 16 bytes, then the plan's
-//   scratch: arrival [2B], group_fill [G], group_start [G + 1], group_lp [G],
-//   and one counter per (sequence, query head) [B][Hq] for the partition
-//   launch's merges.
+//   scratch: arrival [2B], group_fill [G], group_start [G + 1], group_lp [G].
 // num_groups < 0: a plain split-K call, no group tables.
 WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_partitions,
                    int num_groups) {
@@ -35,8 +33,7 @@ WsLayout ws_layout(int num_seqs, int num_heads, int head_dim, int max_partitions
   w.group_fill = up256(w.arrival + (size_t)num_seqs * 2 * sizeof(int));
   w.group_start = up256(w.group_fill + (size_t)num_groups * sizeof(int));
   w.group_lp = up256(w.group_start + (size_t)(num_groups + 1) * sizeof(int));
-  w.merge_cnt = up256(w.group_lp + (size_t)num_groups * sizeof(int));
-  w.total = up256(w.merge_cnt + (size_t)num_seqs * num_heads * sizeof(int));
+  w.total = up256(w.group_lp + (size_t)num_groups * sizeof(int));
   if (!tables) w.total = w.minfo;
   return w;
 }

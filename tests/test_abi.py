@@ -166,9 +166,9 @@ def test_noalloc_rejects_before_touching_the_device(lib):
 
 
 def test_shared_prefix_workspace_holds_group_tables(lib):
-    """The shared-prompt workspace always holds the member records, the
-    plan's group scratch (arrival order, counts, starts, prompt lengths) and
-    a merge counter per (sequence, query head), also for zero groups."""
+    """The shared-prompt workspace always holds the member records and the
+    plan's group scratch (arrival order, counts, starts, prompt lengths),
+    also for zero groups."""
     up = lambda x: (x + 255) // 256 * 256
     B, H, d, maxlen, P = 64, 32, 128, 2048, 256
     parts = maxlen // P + 1                   # one more than the plain split
@@ -181,8 +181,7 @@ def test_shared_prefix_workspace_holds_group_tables(lib):
         group_fill = up(arrival + B * 8)
         group_start = up(group_fill + G * 4)
         group_lp = up(group_start + (G + 1) * 4)
-        merge_cnt = up(group_lp + G * 4)
-        total = up(merge_cnt + B * H * 4)
+        total = up(group_lp + G * 4)
         assert pa.pa_decode_shared_prefix_workspace_bytes(B, H, d, maxlen, P, G) == total, G
     assert pa.pa_decode_shared_prefix_workspace_bytes(B, H, d, maxlen, P, -1) == 0
 
