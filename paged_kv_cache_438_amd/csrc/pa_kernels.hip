@@ -1338,7 +1338,7 @@ struct PArgs {
   URec* urecs;          // [max_units]
   int2* split;          // [num_seqs]: (sequence, partitions) of the sequences to merge
   int4* minfo;          // [num_seqs]: members of the groups, grouped, in sequence order
-  int* arrival;         // [2 num_seqs] scratch when the members do not fit in LDS
+  int* arrival;         // [2 num_seqs] scratch when the members do not fit in LDS: ranks, members
   int* group_fill;      // [num_groups] scratch when the groups do not fit in LDS
   int* group_start;     // [num_groups + 1] scratch, likewise
   int* group_lp;        // [num_groups] scratch, likewise
@@ -1412,7 +1412,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   __shared__ int hist[257];           // bucket counts, then starts (+ total)
   __shared__ int s_tot[kPlanThreads / 64];
   __shared__ int s_split;             // sequences with more than one partition
-  __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_arr[kPlanSeqs], s_mem[kPlanSeqs];
+  __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_rank[kPlanSeqs], s_mem[kPlanSeqs];
   __shared__ int s_gfill[kPlanGroups], s_gstart[kPlanGroups + 1], s_glp[kPlanGroups];
   __shared__ int s_gabs[kPlanGroups];
   __shared__ int s_absorb[17];        // P / max(1, m), m = 0 .. 16
@@ -1450,59 +1450,95 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     }
     return layout_of(a, len_of(s), gi, lp, cnt, s_absorb);
   };
-  int* arrival = s_mem;                // members in arrival order (prompt groups)
+  int* members = s_mem;                // members of the groups, in sequence order within each
   int* gabs = lds_groups ? s_gabs : pa.group_fill;   // reuses the member counts' scratch
   if (shared) {
-    // Members of each group, grouped by a counting sort; each sequence keeps
-    // the slot its atomic gave it (arrival order).
-    for (int s = tid; s < B; s += kPlanThreads) {
-      const int gi = grp_of(s);
-      const int slot = gi >= 0 && gi < NG ? atomicAdd(&gfill[gi], 1) : -1;
-      if (s < kPlanSeqs) s_arr[s] = slot;
-      else pa.arrival[s] = slot;
+    // Members of each group in ascending sequence order, so which member's
+    // own tokens a workgroup streams at which step does not depend on
+    // timing.  The rank of a member among its group's is counted without
+    // atomics: sequences go kPlanThreads at a time, one wave after another;
+    // inside a wave, ballots over the bits of the group index find the lanes
+    // of the same group, and the group's count so far (gfill) is read by all
+    // of them before the lowest of them adds the wave's share.
+    const int lane = tid & 63, wv = tid >> 6;
+    const int gbits = NG > 1 ? 32 - __builtin_clz(NG - 1) : 0;
+    for (int base = 0; base < B; base += kPlanThreads) {
+      const int s = base + tid;
+      const int gi = s < B ? grp_of(s) : -1;
+      const bool in = gi >= 0 && gi < NG;
+      uint64_t same = __builtin_amdgcn_ballot_w64(in);
+      for (int b = 0; b < gbits; ++b) {
+        const bool bit = (gi >> b) & 1;
+        const uint64_t set = __builtin_amdgcn_ballot_w64(bit);
+        same &= bit ? set : ~set;
+      }
+      const int below = __builtin_popcountll(same & ((1ull << lane) - 1));
+      for (int w = 0; w < kPlanThreads / 64; ++w) {
+        if (wv == w && in) {
+          const int before = gfill[gi];
+          if (below == 0) gfill[gi] = before + __builtin_popcountll(same);
+          if (s < kPlanSeqs) s_rank[s] = before + below;
+          else pa.arrival[s] = before + below;
+        }
+        __syncthreads();
+      }
+    }
+    auto validate_groups = [&]() {
+      for (int i = tid; i < NG; i += kPlanThreads) {
+        // A prompt that is not whole blocks, longer than a table can hold,
+        // cut into more partitions than a sequence may have, or shared by
+        // more members than the launch's column chunks cover is out of
+        // contract: it is marked invalid (-1), so its members get NaN rows.
+        const int cnt = gfill[i];
+        const int lp = glp[i];
+        const bool ok = cnt <= pa.max_group_size && lp >= 0 &&
+                        lp <= a.max_len &&
+                        (lp & ((1 << a.bs_log2) - 1)) == 0 && (lp + P - 1) / P <= a.max_parts;
+        glp[i] = ok ? lp : -1;
+        gabs[i] = 0;
+      }
+    };
+    // In LDS the absorbed-token sums have their own array and are cleared
+    // beside the scan; in global memory they reuse the counts, so only after.
+    if (lds_groups) validate_groups();
+    if (NG <= 64) {                     // group starts: one wave's scan
+      if (wv == 0) {
+        const int v = lane < NG ? gfill[lane] : 0;
+        int incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int t = __shfl_up(incl, off);
+          if (lane >= off) incl += t;
+        }
+        if (lane < NG) gstart[lane] = incl - v;
+        if (lane == 63) gstart[NG] = incl;
+      }
+    } else {
+      block_exclusive_scan(gfill, gstart, NG, s_tot);
     }
     __syncthreads();
-    block_exclusive_scan(gfill, gstart, NG, s_tot);
-    __syncthreads();
-    for (int i = tid; i < NG; i += kPlanThreads) {
-      // A prompt that is not whole blocks, longer than a table can hold, cut
-      // into more partitions than a sequence may have, or shared by more
-      // members than the launch's column chunks cover is out of contract:
-      // it is marked invalid (-1), so its members get NaN rows.
-      const int cnt = gfill[i];
-      const int lp = glp[i];
-      const bool ok = cnt <= pa.max_group_size && lp >= 0 &&
-                      lp <= a.max_len &&
-                      (lp & ((1 << a.bs_log2) - 1)) == 0 && (lp + P - 1) / P <= a.max_parts;
-      glp[i] = ok ? lp : -1;
-      gabs[i] = 0;
+    if (!lds_groups) {
+      validate_groups();
+      __syncthreads();
     }
-    // Members in ascending sequence order, so which member's own tokens a
-    // workgroup streams at which step does not depend on timing: first in
-    // arrival order (mem), then each placed at its rank among its group's
-    // members with its record: sequence, absorbed own tokens, flags.
+    // Each member at its place: the member list, and its record (sequence,
+    // absorbed own tokens, flags); gabs[gi] <- absorbed own tokens of the
+    // group per column chunk (at most about P by the absorption bound).
     const int nmem = gstart[NG];
     int* mem = nmem <= kPlanSeqs ? s_mem : pa.arrival + B;
     for (int s = tid; s < B; s += kPlanThreads) {
       const int gi = grp_of(s);
-      if (gi >= 0 && gi < NG) mem[gstart[gi] + (s < kPlanSeqs ? s_arr[s] : pa.arrival[s])] = s;
-    }
-    arrival = mem;
-    __syncthreads();
-    // gabs[gi] <- absorbed own tokens of the group per column chunk (at most
-    // about P by the absorption bound), summed while the records are written.
-    for (int x = tid; x < nmem; x += kPlanThreads) {
-      const int s = arrival[x];
-      const int gi = grp_of(s);
+      if (gi < 0 || gi >= NG) continue;
       const int lo = gstart[gi], hi = gstart[gi + 1];
-      int rank = 0;
-      for (int y = lo; y < hi; ++y) rank += arrival[y] < s;
+      const int at = lo + (s < kPlanSeqs ? s_rank[s] : pa.arrival[s]);
+      mem[at] = s;
       const SeqLayout ml = layout(s);
       const bool own = ml.absorbed && !ml.bad;
-      pa.minfo[lo + rank] = make_int4(s, own ? ml.lp : 0, own ? ml.len : 0,
-                                      (ml.nparts == 1 ? kUnitDirect : 0) | (ml.bad ? kUnitBad : 0));
+      pa.minfo[at] = make_int4(s, own ? ml.lp : 0, own ? ml.len : 0,
+                               (ml.nparts == 1 ? kUnitDirect : 0) | (ml.bad ? kUnitBad : 0));
       if (own) atomicAdd(&gabs[gi], (ml.len - ml.lp) / (((hi - lo) * a.group + 15) / 16));
     }
+    members = mem;
     __syncthreads();
   }
   // Units hold up to 2P tokens (a last prompt partition with absorbed own
@@ -1550,7 +1586,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       r.first = gstart[gi];
       r.cnt = gstart[gi + 1] - r.first;
       r.lp = glp[gi];
-      r.ts = arrival[r.first];                   // any member: all share the prompt's blocks
+      r.ts = members[r.first];                   // any member: all share the prompt's blocks
       r.pf = 0;
       r.tb = 0;
       r.te = P;
