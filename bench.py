@@ -440,7 +440,7 @@ def main() -> int:
             ident = perm.to(torch.int32).reshape(-1, 1).contiguous()
     else:
         kp, vp = d(case.k_pool, dt), d(case.v_pool, dt)
-        kn, vn = d(case.k_new, dt), d(case.v_new, dt)
+    kn, vn = d(case.k_new, dt), d(case.v_new, dt)
     out = torch.empty_like(q)
     maxlen = int(case.context_lens.max())
     scale = float(case.scale)
@@ -489,10 +489,13 @@ def main() -> int:
                                 scale=scale, out=out, workspace=ws, shared_kv=shared,
                                 valu_only=args.valu_only)
 
-    # A step is the new token's cache write and the decode; a contiguous
-    # cache has no paged write, so its step is the decode alone.
+    # A step is the new token's cache write and the decode.
     def write():
-        if not args.contiguous:
+        if args.through_table:                  # the paged write through the same table
+            pa.pa_cache_write(kc, vc, kn, vn, ident, ln)
+        elif args.contiguous:
+            pa.pa_cache_write_contiguous(kc, vc, kn, vn, ln)
+        else:
             pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
 
     def step():
@@ -529,8 +532,9 @@ def main() -> int:
     if args.through_table:
         dec_bytes += 4 * w.num_seqs
         logical_bytes += 4 * w.num_seqs
-    cw_bytes = 0 if args.contiguous else \
-        4 * w.num_seqs * w.num_kv_heads * w.head_dim * e + 4 * 2 * w.num_seqs
+    # The write reads both new rows and writes them, plus the lengths and (paged) one table entry.
+    cw_bytes = 4 * w.num_seqs * w.num_kv_heads * w.head_dim * e + \
+        4 * (1 if args.contiguous and not args.through_table else 2) * w.num_seqs
     step_bytes = dec_bytes + cw_bytes
     ms_step = elapsed * 1e3 / K
     value = step_bytes * K / elapsed / 1e9
@@ -592,7 +596,8 @@ def main() -> int:
                                  "contiguous cache through an identity table"
                                  if args.through_table else "contiguous cache"
                                  if args.contiguous else "paged pool"),
-                   "step": "decode (contiguous cache, no paged write)" if args.contiguous
+                   "step": "pa_cache_write_contiguous + decode"
+                   if args.contiguous and not args.through_table
                    else "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
         "max_abs_err": max_err,
         "tolerance": tol,

@@ -312,6 +312,19 @@ int pa_decode_contiguous(void* out, const void* q, const void* k_cache, const vo
                          void* stream);
 
 /*
+ * pa_cache_write_contiguous -- pa_cache_write for the contiguous cache of
+ * pa_decode_contiguous: for every sequence with 1 <= L <= max_len
+ * (L = context_lens[s], which already counts the new token) and every KV
+ * head g, the head_dim elements of k_new[s][g] and v_new[s][g] are copied,
+ * bit for bit, to row L-1 of k_cache[s][g] and v_cache[s][g]
+ * ([num_seqs][num_kv_heads][max_len][head_dim]).  Other lengths write
+ * nothing; no other byte changes.  num_seqs == 0 is a no-op.
+ */
+int pa_cache_write_contiguous(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                              const int32_t* context_lens, int num_seqs, int num_kv_heads,
+                              int head_dim, int max_len, int dtype, void* stream);
+
+/*
  * pa_copy_blocks -- copy whole blocks of both pools, every KV head:
  * for i < num_pairs, block pairs[i][1] of k_pool and v_pool receives the
  * bytes of block pairs[i][0].  This is the private copy a shared, partly

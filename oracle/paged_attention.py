@@ -187,6 +187,26 @@ def cache_write(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
     return kp, vp
 
 
+def cache_write_contiguous(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray,
+                           v_new: np.ndarray, context_lens: np.ndarray
+                           ) -> Tuple[np.ndarray, np.ndarray]:
+    """The same write for the pre-paging layout, where each request owns one
+    contiguous region of max_len rows per KV head ("IO-5 vLLM Paged
+    Attention", section 1): the newest token (position L-1, R4) goes to row
+    L-1 of k_cache[s][g] and v_cache[s][g], [B][Hkv][max_len][d], every KV
+    head.  L = 0 writes nothing (R3); a length past max_len does not fit and
+    writes nothing either.  Bytewise; returns new caches."""
+    kc, vc = k_cache.copy(), v_cache.copy()
+    max_len = k_cache.shape[2]
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        if L < 1 or L > max_len:
+            continue
+        kc[s, :, L - 1, :] = k_new[s]
+        vc[s, :, L - 1, :] = v_new[s]
+    return kc, vc
+
+
 def contiguous_attention(q: np.ndarray, K_seqs: List[np.ndarray], V_seqs: List[np.ndarray],
                          scale, dtype: str, num_kv_heads: int) -> np.ndarray:
     """Attention over per-sequence contiguous K/V ([L][Hkv][d] each), the

@@ -39,6 +39,7 @@ _SIGNATURES = {
                           _c_void_p]),
     "pa_decode_splitk_noalloc": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
                                  [_c_float, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
+    "pa_cache_write_contiguous": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 + [_c_void_p]),
     "pa_decode_contiguous": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 +
                              [_c_float, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
                               _c_void_p]),
@@ -269,6 +270,38 @@ def pa_decode_splitk_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torc
     return out
 
 
+def _contiguous_shape(k_cache, v_cache) -> Tuple[int, int, int, int]:
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be "
+                         "[num_seqs][num_kv_heads][max_len][head_dim]")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache must share one dtype")
+    return tuple(k_cache.shape)
+
+
+def pa_cache_write_contiguous(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                              v_new: torch.Tensor, context_lens: torch.Tensor,
+                              stream=None) -> None:
+    """Store each sequence's newest token (row context_lens[s]-1) into its
+    region of a contiguous cache, in place.  See pa_cache_write_contiguous in
+    include/pa.h."""
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)):
+        _dev(t, n)
+    B, Hkv, max_len, d = _contiguous_shape(k_cache, v_cache)
+    if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+    if not (k_cache.dtype == k_new.dtype == v_new.dtype):
+        raise TypeError("caches and new rows must share one dtype")
+    _dev(context_lens, "context_lens", torch.int32)
+    if context_lens.shape != (B,):
+        raise ValueError("context_lens must be [num_seqs]")
+    st = load().pa_cache_write_contiguous(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
+                                          v_new.data_ptr(), context_lens.data_ptr(), B, Hkv, d,
+                                          max_len, _DTYPES.get(k_cache.dtype, -1),
+                                          _stream(k_cache.device, stream))
+    _check(st, "pa_cache_write_contiguous")
+
+
 def pa_decode_contiguous(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                          context_lens: torch.Tensor, scale: float, partition_size: int = 0,
                          out: Optional[torch.Tensor] = None,
@@ -280,10 +313,7 @@ def pa_decode_contiguous(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     See pa_decode_contiguous in include/pa.h."""
     for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev(t, n)
-    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must both be "
-                         "[num_seqs][num_kv_heads][max_len][head_dim]")
-    B, Hkv, max_len, d = k_cache.shape
+    B, Hkv, max_len, d = _contiguous_shape(k_cache, v_cache)
     if q.dim() != 3 or q.shape[0] != B or q.shape[2] != d:
         raise ValueError("q must be [num_seqs][num_heads][head_dim] with k_cache's num_seqs "
                          "and head_dim")

@@ -168,6 +168,38 @@ int pa_cache_write(void* k_pool, void* v_pool, const void* k_new, const void* v_
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.num_blocks = num_blocks;
   p.dtype = dtype;
+  p.max_len = 0;
+  return finish_launch(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
+}
+
+int pa_cache_write_contiguous(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                              const int32_t* context_lens, int num_seqs, int num_kv_heads,
+                              int head_dim, int max_len, int dtype, void* stream) {
+  if (max_len <= 0) return pa_fail(PA_ERR_INVALID_ARG, "max_len must be > 0 (got %d)", max_len);
+  // The checks of a paged call with one block of max_len rows per sequence.
+  int st = check_common(num_seqs, num_kv_heads, head_dim, 1, max_len, num_seqs > 0 ? num_seqs : 1,
+                        dtype);
+  if (st) return st;
+  if (num_seqs == 0) return pa_ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !context_lens)
+    return pa_fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return pa_fail(PA_ERR_INVALID_ARG, "caches and new rows must be 16-byte aligned");
+  pa::CacheWriteParams p;
+  p.k_pool = k_cache;
+  p.v_pool = v_cache;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.block_tables = nullptr;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = 1;
+  p.max_blocks_per_seq = 1;
+  p.num_blocks = num_seqs;
+  p.dtype = dtype;
+  p.max_len = max_len;
   return finish_launch(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -1731,12 +1731,15 @@ struct CArgs {
   uint8_t* v_pool;
   const uint8_t* k_new;
   const uint8_t* v_new;
-  const int32_t* tables;
+  const int32_t* tables;   // nullptr: a contiguous cache [B][Hkv][max_len][d]
   const int32_t* lens;
   int num_seqs, num_kv_heads, row_chunks, row_bytes, bs_log2, max_blocks, num_blocks;
+  int max_len;             // longest valid length (max_blocks << bs_log2 when paged)
 };
 
-// One thread per 16-byte chunk of a (sequence, KV head) row; copies K and V.
+// One thread per 16-byte chunk of a (sequence, KV head) row; copies K and V
+// into row L-1 of the sequence: through its table, or in its contiguous
+// region.
 __global__ __launch_bounds__(256) void k_cache_write(const CArgs a) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.num_seqs * a.num_kv_heads * a.row_chunks) return;
@@ -1745,13 +1748,18 @@ __global__ __launch_bounds__(256) void k_cache_write(const CArgs a) {
   const int g = sg % a.num_kv_heads;
   const int s = sg / a.num_kv_heads;
   const int len = a.lens[s];
-  if (len < 1 || len > (a.max_blocks << a.bs_log2)) return;
+  if (len < 1 || len > a.max_len) return;
   const int pos = len - 1;
-  const int phys = a.tables[(size_t)s * a.max_blocks + (pos >> a.bs_log2)];
-  if ((unsigned)phys >= (unsigned)a.num_blocks) return;
-  const size_t tile = (size_t)a.row_bytes << a.bs_log2;
-  const size_t dst = ((size_t)phys * a.num_kv_heads + g) * tile +
-                     (size_t)(pos & ((1 << a.bs_log2) - 1)) * a.row_bytes + (size_t)c * 16;
+  size_t dst;
+  if (a.tables == nullptr) {
+    dst = ((size_t)sg * a.max_len + pos) * a.row_bytes + (size_t)c * 16;
+  } else {
+    const int phys = a.tables[(size_t)s * a.max_blocks + (pos >> a.bs_log2)];
+    if ((unsigned)phys >= (unsigned)a.num_blocks) return;
+    const size_t tile = (size_t)a.row_bytes << a.bs_log2;
+    dst = ((size_t)phys * a.num_kv_heads + g) * tile +
+          (size_t)(pos & ((1 << a.bs_log2) - 1)) * a.row_bytes + (size_t)c * 16;
+  }
   const size_t src = (size_t)sg * a.row_bytes + (size_t)c * 16;
   *reinterpret_cast<uint4*>(a.k_pool + dst) = *reinterpret_cast<const uint4*>(a.k_new + src);
   *reinterpret_cast<uint4*>(a.v_pool + dst) = *reinterpret_cast<const uint4*>(a.v_new + src);
@@ -2246,9 +2254,11 @@ hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
   ca.num_kv_heads = p.num_kv_heads;
   ca.row_bytes = p.head_dim * eb;
   ca.row_chunks = ca.row_bytes / 16;
-  ca.bs_log2 = ilog2(p.block_size);
+  const bool contiguous = p.block_tables == nullptr;
+  ca.bs_log2 = contiguous ? 0 : ilog2(p.block_size);
   ca.max_blocks = p.max_blocks_per_seq;
   ca.num_blocks = p.num_blocks;
+  ca.max_len = contiguous ? p.max_len : p.max_blocks_per_seq * p.block_size;
   const long long total = (long long)p.num_seqs * p.num_kv_heads * ca.row_chunks;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 255) / 256);

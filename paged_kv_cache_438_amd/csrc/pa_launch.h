@@ -47,7 +47,7 @@ struct CacheWriteParams {
   void* v_pool;
   const void* k_new;
   const void* v_new;
-  const int32_t* block_tables;
+  const int32_t* block_tables;  // nullptr: a contiguous cache of max_len rows per sequence
   const int32_t* context_lens;
   int num_seqs;
   int num_kv_heads;
@@ -56,6 +56,7 @@ struct CacheWriteParams {
   int max_blocks_per_seq;
   int num_blocks;
   int dtype;
+  int max_len;             // contiguous cache: rows per (sequence, KV head); 0 when paged
 };
 
 // Byte offsets of the parts of the split-K workspace (pa_workspace.cpp).

@@ -15,8 +15,8 @@ import struct
 
 import numpy as np
 
-from synthetic import (GQA70B, LLAMA7B, LONG_BS512, SHARED_PREFIX, TINY, make_case,
-                       small_variant, to_storage)
+from synthetic import (GQA70B, LLAMA7B, LONG_BS512, SHARED_PREFIX, TINY, NAN_BITS,
+                       contiguous_cache, make_case, small_variant, to_storage)
 
 GOLDEN = pathlib.Path(__file__).parent / "golden"
 
@@ -360,7 +360,33 @@ def pin_cache_write_round_trip(O):
         assert vp1.tobytes() == c.v_pool.tobytes(), w.name
 
 
+def pin_contiguous_cache_write(O):
+    """The contiguous layout's write: putting each sequence's newest token
+    into a cache whose row L-1 holds NaN gives back the cache the generator
+    laid out from its own logical rows, byte for byte; lengths of 0 or past
+    the region change nothing."""
+    for w in (TINY, small_variant(GQA70B), small_variant(LLAMA7B)):
+        c = make_case(w, keep_logical=True)
+        max_len = int(c.context_lens.max()) + 3
+        kc, vc = contiguous_cache(c, max_len)
+        kp0, vp0 = kc.copy(), vc.copy()
+        for s, L in enumerate(c.context_lens):
+            if L >= 1:
+                kp0[s, :, L - 1] = NAN_BITS[w.dtype]
+                vp0[s, :, L - 1] = NAN_BITS[w.dtype]
+        assert kp0.tobytes() != kc.tobytes()
+        k1, v1 = O.cache_write_contiguous(kp0, vp0, c.k_new, c.v_new, c.context_lens)
+        assert k1.tobytes() == kc.tobytes() and v1.tobytes() == vc.tobytes(), w.name
+        # lengths that write nothing
+        lens = c.context_lens.copy()
+        lens[:] = 0
+        lens[-1] = max_len + 1
+        k2, v2 = O.cache_write_contiguous(kp0, vp0, c.k_new, c.v_new, lens)
+        assert k2.tobytes() == kp0.tobytes() and v2.tobytes() == vp0.tobytes(), w.name
+
+
 ALL_PINS = [pin_page_table_example, pin_page_table_example_cache_write, pin_pages_arithmetic,
             pin_brute_force, pin_closed_forms, pin_contiguous_equality,
             pin_permutation_invariance, pin_shared_equals_duplicated,
-            pin_gqa_equals_repeated_mha, pin_partition_merge, pin_cache_write_round_trip]
+            pin_gqa_equals_repeated_mha, pin_partition_merge, pin_cache_write_round_trip,
+            pin_contiguous_cache_write]

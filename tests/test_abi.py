@@ -142,6 +142,22 @@ def test_contiguous_rejects(lib):
     assert call(B=0, out=0, k=0, ln=0) == 0    # nothing to do
 
 
+def test_contiguous_write_rejects(lib):
+    def call(B=4, Hkv=2, d=128, max_len=100, dtype=1, kc=P, kn=P, ln=P):
+        return lib.pa_cache_write_contiguous(kc, P, kn, P, ln, B, Hkv, d, max_len, dtype, None)
+
+    assert call(max_len=0) == 2
+    assert call(d=80) == 3
+    assert call(dtype=7) == 3
+    assert call(Hkv=0) == 2
+    assert call(B=-1) == 2
+    assert call(kc=0) == 1
+    assert call(ln=0) == 1
+    assert call(kn=P + 8) == 2
+    assert call(max_len=1 << 30) == 2
+    assert call(B=0, kc=0, kn=0, ln=0) == 0
+
+
 def test_noalloc_rejects_before_touching_the_device(lib):
     """pa_decode_splitk_noalloc checks its arguments like pa_decode_splitk
     and refuses sizes whose workspace exceeds the static scratch, all before

@@ -19,7 +19,8 @@ import torch
 
 import oracle
 import paged_kv_cache_438_amd as pa
-from synthetic import GQA70B, LLAMA7B, WORKLOADS, Workload, contiguous_cache, make_case, small_variant
+from synthetic import (GQA70B, LLAMA7B, NAN_BITS, WORKLOADS, Workload, contiguous_cache, make_case,
+                       small_variant)
 from tests.gpu_util import TOL, DevCase, dev_array, host_bits, host_f64, note
 
 pytestmark = pytest.mark.gpu
@@ -151,3 +152,38 @@ def test_contiguous_full_size_bitwise_equal_to_paged(w, P):
         _check_close(g[s:s + 1], r, w.dtype, f"{w.name}/seq {s}")
     del kc, vc
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_contiguous_cache_write_bit_exact(w):
+    """pa_cache_write_contiguous against the oracle's write, byte for byte:
+    into a cache whose rows L-1 hold NaN, then with lengths of 0 and past the
+    region (nothing written); then the written cache decodes like the
+    oracle."""
+    c = make_case(w, keep_logical=True)
+    max_len = int(c.context_lens.max()) + 5
+    kc, vc = contiguous_cache(c, max_len)
+    k0, v0 = kc.copy(), vc.copy()
+    for s_, L in enumerate(c.context_lens):
+        if L >= 1:
+            k0[s_, :, L - 1] = NAN_BITS[w.dtype]
+            v0[s_, :, L - 1] = NAN_BITS[w.dtype]
+    note(f"contiguous write: {w.name} max_len={max_len} lens={c.context_lens.tolist()}")
+    dk, dv = dev_array(k0, w.dtype), dev_array(v0, w.dtype)
+    kn, vn = dev_array(c.k_new, w.dtype), dev_array(c.v_new, w.dtype)
+    d = DevCase(c)
+    pa.pa_cache_write_contiguous(dk, dv, kn, vn, d.lens)
+    torch.cuda.synchronize()
+    ek, ev = oracle.cache_write_contiguous(k0, v0, c.k_new, c.v_new, c.context_lens)
+    assert host_bits(dk).tobytes() == ek.tobytes()
+    assert host_bits(dv).tobytes() == ev.tobytes()
+    got = pa.pa_decode_contiguous(d.q, dk, dv, d.lens, scale=float(c.scale))
+    torch.cuda.synchronize()
+    _check_close(host_f64(got), _contig_oracle(c), w.dtype, f"{w.name}/write+decode")
+    # lengths that write nothing
+    lens = np.zeros_like(c.context_lens)
+    lens[-1] = max_len + 1
+    pa.pa_cache_write_contiguous(dk, dv, kn, vn, dev_array(lens))
+    torch.cuda.synchronize()
+    assert host_bits(dk).tobytes() == ek.tobytes()
+    assert host_bits(dv).tobytes() == ev.tobytes()

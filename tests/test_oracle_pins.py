@@ -69,6 +69,17 @@ def _cache_write_at_L(k_pool, v_pool, k_new, v_new, block_tables, context_lens, 
     return kp, vp
 
 
+def _cache_write_contiguous_at_L(k_cache, v_cache, k_new, v_new, context_lens):
+    kc, vc = k_cache.copy(), v_cache.copy()
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        if L < 1 or L >= k_cache.shape[2]:
+            continue
+        kc[s, :, L, :] = k_new[s]                             # off by one
+        vc[s, :, L, :] = v_new[s]
+    return kc, vc
+
+
 def _decode_gqa_modulo(q, k_pool, v_pool, block_tables, context_lens, scale, block_size,
                        dtype, pairs=None):
     B, Hq, d = q.shape
@@ -99,6 +110,7 @@ MUTANTS = {
     "max_not_subtracted": ("softmax_attention", _softmax_no_max),
     "bf16_widen_shift": ("widen", _widen_bad_bf16),
     "cache_write_at_L": ("cache_write", _cache_write_at_L),
+    "contiguous_write_at_L": ("cache_write_contiguous", _cache_write_contiguous_at_L),
     "gqa_modulo_mapping": ("decode", _decode_gqa_modulo),
     "k_v_swapped": ("decode", _decode_kv_swapped),
 }
