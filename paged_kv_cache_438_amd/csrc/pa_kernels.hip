@@ -1655,6 +1655,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Partitions whose accumulators one reduce wave loads at once.
+#ifndef PA_REDUCE_INFLIGHT
+#define PA_REDUCE_INFLIGHT 8
+#endif
+
 // One wave per (sequence, head) of the sequences the plan listed as split
 // merges their partitions: with M = max_p m_p,
 //   out = sum_p 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p.
@@ -1666,7 +1671,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_reduce(const KArgs a) {
   constexpr int EPL = D / 64;          // head-dim elements per lane (1 or 2)
-  constexpr int U = 8;                 // partition loads in flight
+  constexpr int U = PA_REDUCE_INFLIGHT;   // partition loads in flight
   const int lane = threadIdx.x & 63;
   const int total = a.n_units[1] * a.num_heads;
   for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < total; it += gridDim.x * 4) {
