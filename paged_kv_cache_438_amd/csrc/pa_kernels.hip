@@ -144,6 +144,20 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: within each 16-lane DPP
+// row shift-and-add by 1, 2, 4 and 8 (lanes without a source add 0), then
+// carry row 0's total into row 1 and row 2's into row 3 (row_bcast:15), and
+// rows 0-1's total into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return v;
+}
+
 // Sum over the LPR consecutive lanes of a row group; every lane of the group
 // receives the total.  Inside a 16-lane DPP row: swap neighbours, swap pairs,
 // mirror halves of 8, mirror the row of 16; groups of 32 add the other row.
@@ -1097,12 +1111,7 @@ void k_decode_mfma(const KArgs a) {
         st_te = mrec.z;
       }
       const int cnt = st_te > st_tb ? (st_te - st_tb + 15) >> 4 : 0;
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
+      const int incl = wave_inclusive_sum(cnt);
       st_first = incl - cnt;
       nsteps = __builtin_amdgcn_readlane(incl, 63);
     }
@@ -1359,12 +1368,7 @@ __device__ __forceinline__ void block_exclusive_scan(const int* src, int* dst, i
   int carry = 0;
   for (int base = 0; base < n; base += kPlanThreads) {
     const int v = base + tid < n ? src[base + tid] : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
-    }
+    const int incl = wave_inclusive_sum(v);
     if (lane == 63) s_tot[wv] = incl;
     __syncthreads();
     int before = carry;
@@ -1413,6 +1417,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   __shared__ int s_tot[kPlanThreads / 64];
   __shared__ int s_split;             // sequences with more than one partition
   __shared__ int s_len[kPlanSeqs], s_grp[kPlanSeqs], s_rank[kPlanSeqs], s_mem[kPlanSeqs];
+  // Prompt groups: each sequence's layout as the member phase computed it,
+  // its partitions (-1: out of contract) and prompt length, for the passes.
+  __shared__ int s_npc[kPlanSeqs], s_lpc[kPlanSeqs];
   __shared__ int s_gfill[kPlanGroups], s_gstart[kPlanGroups + 1], s_glp[kPlanGroups];
   __shared__ int s_gabs[kPlanGroups];
   __shared__ int s_absorb[17];        // P / max(1, m), m = 0 .. 16
@@ -1504,12 +1511,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     if (NG <= 64) {                     // group starts: one wave's scan
       if (wv == 0) {
         const int v = lane < NG ? gfill[lane] : 0;
-        int incl = v;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int t = __shfl_up(incl, off);
-          if (lane >= off) incl += t;
-        }
+        const int incl = wave_inclusive_sum(v);
         if (lane < NG) gstart[lane] = incl - v;
         if (lane == 63) gstart[NG] = incl;
       }
@@ -1527,12 +1529,16 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     const int nmem = gstart[NG];
     int* mem = nmem <= kPlanSeqs ? s_mem : pa.arrival + B;
     for (int s = tid; s < B; s += kPlanThreads) {
+      const SeqLayout ml = layout(s);
+      if (s < kPlanSeqs) {
+        s_npc[s] = ml.bad ? -1 : ml.nparts;
+        s_lpc[s] = ml.lp;
+      }
       const int gi = grp_of(s);
       if (gi < 0 || gi >= NG) continue;
       const int lo = gstart[gi], hi = gstart[gi + 1];
       const int at = lo + (s < kPlanSeqs ? s_rank[s] : pa.arrival[s]);
       mem[at] = s;
-      const SeqLayout ml = layout(s);
       const bool own = ml.absorbed && !ml.bad;
       pa.minfo[at] = make_int4(s, own ? ml.lp : 0, own ? ml.len : 0,
                                (ml.nparts == 1 ? kUnitDirect : 0) | (ml.bad ? kUnitBad : 0));
@@ -1541,6 +1547,20 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
     members = mem;
     __syncthreads();
   }
+  // A sequence's layout in the passes: with prompt groups, from what the
+  // member phase kept (a shorter chain of LDS reads than layout()).
+  auto seq_layout = [&](int s) {
+    if (!shared || s >= kPlanSeqs) return layout(s);
+    SeqLayout r;
+    const int np = s_npc[s];
+    r.bad = np < 0;
+    r.nparts = r.bad ? 0 : np;
+    r.lp = r.bad ? 0 : s_lpc[s];
+    r.len = r.bad ? 0 : s_len[s];
+    r.np_pre = a.part_div.div(r.lp + P - 1);
+    r.absorbed = false;                 // not needed by the passes
+    return r;
+  };
   // Units hold up to 2P tokens (a last prompt partition with absorbed own
   // tokens); buckets split [0, 2P] evenly, largest first.
   const float bucket_scale = 128.f / (float)P;
@@ -1598,7 +1618,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       put(r.lp - r.tb + gabs[gi], r, 1);
     }
     for (int s = tid; s < B; s += kPlanThreads) {
-      const SeqLayout lay = layout(s);
+      const SeqLayout lay = seq_layout(s);
       const int own = lay.nparts - lay.np_pre;
       if (pass == 0 && lay.nparts > 1) pa.split[atomicAdd(&s_split, 1)] = make_int2(s, lay.nparts);
       URec r;
