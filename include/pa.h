@@ -160,8 +160,10 @@ size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_di
 
 /*
  * pa_decode_splitk -- the same result as pa_decode, computed in three
- * launches for long contexts: each sequence's tokens are cut into partitions
- * of `partition_size` tokens (a positive multiple of 16).  A one-workgroup
+ * launches for long contexts: each sequence's L tokens are cut into
+ * ceil(L / partition_size) partitions of equal length, rounded up to whole
+ * 16-token steps, the last holding the rest (so none exceeds
+ * `partition_size`, a positive multiple of 16).  A one-workgroup
  * planning launch lists the (sequence, partition) pairs longest first; the
  * partition launch takes them in that order and computes, per (sequence,
  * head, partition), the partition's maximum score m, sum of exp(score - m)
@@ -251,7 +253,8 @@ size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int 
  * heads per KV head dividing 16); that partition then streams each absorbed
  * member's tokens too, seen only by that member's columns, so it never
  * holds more than 2 * partition_size tokens.  Other members' own tokens,
- * and ungrouped sequences, are cut into partitions of their own.  A member
+ * and ungrouped sequences, are cut into partitions of their own, balanced
+ * as in pa_decode_splitk.  A member
  * whose only partition is the absorbing one gets its output written
  * directly; otherwise partials are merged in fixed order as in
  * pa_decode_splitk.  Results are deterministic: the plan sorts each group's

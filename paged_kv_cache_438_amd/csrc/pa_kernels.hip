@@ -1389,13 +1389,21 @@ constexpr int kPlanGroups = 1024;
 // Runs of full partitions the plan queues for whole waves to write.
 constexpr int kPlanLongRuns = 256;
 
+// A sequence's own tokens in ceil(len / P) parts of equal length (whole
+// 16-token steps, at most P tokens, the last holding the rest) rather than
+// parts of P tokens and a remainder: the longest units are then no longer
+// than they need to be (1: on).
+#ifndef PA_BALANCED_PARTS
+#define PA_BALANCED_PARTS 1
+#endif
 // Record i of a run of full partitions starting with record r: partition
 // slot + i, token range shifted by i partitions.
-__device__ __forceinline__ URec run_record(const URec& r, int i, int P) {
+__device__ __forceinline__ URec run_record(const URec& r, int i) {
+  const int stride = r.te - r.tb;       // every record of a run spans the same tokens
   URec x = r;
   x.pf += i;
-  x.tb += i * P;
-  x.te += i * P;
+  x.tb += i * stride;
+  x.te += i * stride;
   return x;
 }
 
@@ -1596,7 +1604,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
           return;
         }
       }
-      for (int i = 0; i < n; ++i) pa.urecs[at + i] = run_record(r, i, P);
+      for (int i = 0; i < n; ++i) pa.urecs[at + i] = run_record(r, i);
     };
     for (int gi = tid; gi < NG; gi += kPlanThreads) {
       const int np = prompt_parts(gi);
@@ -1632,12 +1640,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       }
       if (own > 0) {
         const int flags = lay.nparts == 1 ? kUnitDirect : 0;
+#if PA_BALANCED_PARTS
+        const int span = lay.len - lay.lp;
+        const int S = own == 1 ? P : ((span + own - 1) / own + 15) & ~15;
+#else
+        const int S = P;
+#endif
         r.pf = lay.np_pre | flags;
         r.tb = lay.lp;
-        r.te = lay.lp + P;
-        put(P, r, own - 1);                      // full partitions
+        r.te = lay.lp + S;
+        put(S, r, own - 1);                      // full parts
         r.pf = (lay.np_pre + own - 1) | flags;
-        r.tb = lay.lp + (own - 1) * P;
+        r.tb = lay.lp + (own - 1) * S;
         r.te = lay.len;
         put(lay.len - r.tb, r, 1);
       }
@@ -1649,7 +1663,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
       const int nl = min(s_nlong, kPlanLongRuns);
       for (int li = tid >> 6; li < nl; li += kPlanThreads / 64)
         for (int i = tid & 63; i < s_ln[li]; i += 64)
-          pa.urecs[s_lat[li] + i] = run_record(s_lrec[li], i, P);
+          pa.urecs[s_lat[li] + i] = run_record(s_lrec[li], i);
     }
     if (pass == 0) {
       // bucket counts -> bucket starts; hist[256] = number of units
