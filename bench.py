@@ -40,7 +40,9 @@ DEFAULT_ENTRY = {"llama2_7b": ("single", None), "long_bs512": ("splitk", 512),
                  "gqa_70b": ("splitk", 8192), "shared_prefix": ("shared", 2048),
                  "tiny": ("single", None)}
 ENTRY_NAME = {"single": "pa_decode", "splitk": "pa_decode_splitk",
-              "shared": "pa_decode_shared_prefix", "contiguous": "pa_decode_contiguous"}
+              "shared": "pa_decode_shared_prefix", "contiguous": "pa_decode_contiguous",
+              "splitk_combined": "pa_write_decode_splitk",
+              "shared_combined": "pa_write_decode_shared_prefix"}
 
 
 def log(*a):
@@ -333,6 +335,12 @@ def main() -> int:
                     help="plain cached K/V loads (the shared-blocks policy) even without sharing")
     ap.add_argument("--valu-only", action="store_true",
                     help="grouped heads on the vector ALUs instead of the matrix cores")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="split-K and shared-prompt entries: write the new token with "
+                         "pa_cache_write and time the decode call alone, instead of the "
+                         "default single call (pa_write_decode_splitk or "
+                         "pa_write_decode_shared_prefix) that writes in the plan's launch and "
+                         "is timed as the whole step")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the read-probe measurement reported beside the roofline")
     ap.add_argument("--block-ops", action="store_true",
@@ -395,6 +403,10 @@ def main() -> int:
         P = args.partition or (w.partition_size or 1024) if entry != "single" else None
     elif args.partition:
         P = args.partition
+    if args.separate_write and (entry == "single" or args.contiguous):
+        raise SystemExit("--separate-write needs a split-K or shared-prompt entry on a paged pool")
+    # Split entries on a paged pool run the step as one call by default.
+    args.combined = entry != "single" and not args.contiguous and not args.separate_write
     t = time.perf_counter()
     case = make_case(w, seed=args.seed, keep_logical=args.contiguous)
     log(f"bench: generated {w.name} seed={case.seed} in {time.perf_counter() - t:.1f} s; "
@@ -498,9 +510,23 @@ def main() -> int:
         else:
             pa.pa_cache_write(kp, vp, kn, vn, tb, ln)
 
+    # The same step as one call: the write runs in the plan's launch.
+    def combined():
+        if entry == "shared":
+            pa.pa_write_decode_shared_prefix(q, kp, vp, kn, vn, tb, ln, seq_group, group_prefix,
+                                             max_group, P, maxlen, scale=scale, out=out,
+                                             workspace=ws, shared_kv=shared)
+        else:
+            pa.pa_write_decode_splitk(q, kp, vp, kn, vn, tb, ln, partition_size=P,
+                                      max_context_len=maxlen, scale=scale, out=out,
+                                      workspace=ws, shared_kv=shared, valu_only=args.valu_only)
+
     def step():
-        write()
-        decode()
+        if args.combined:
+            combined()
+        else:
+            write()
+            decode()
 
     for _ in range(args.warmup):
         step()
@@ -511,6 +537,11 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        if args.combined:
+            evs[i][0].record()
+            combined()
+            evs[i][1].record()
+            continue
         write()
         evs[i][0].record()
         decode()
@@ -539,7 +570,9 @@ def main() -> int:
     ms_step = elapsed * 1e3 / K
     value = step_bytes * K / elapsed / 1e9
     tokens = kv_token_count(case)
-    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    # The timed call: the decode, or (split entries, one call) the whole step.
+    timed_bytes = step_bytes if args.combined else dec_bytes
+    achieved = timed_bytes / (dec_ms * 1e-3) / 1e9
 
     # The output of the last timed step against the fp64 oracle, every
     # (sequence, head) row, within the storage dtype's max-abs bound.
@@ -558,6 +591,8 @@ def main() -> int:
 
     traffic = None
     entry_key = entry if args.through_table else "contiguous" if args.contiguous else entry
+    if args.combined:
+        entry_key += "_combined"
     tf = ROOT / "profiles" / f"traffic_{w.name}_{entry_key}.json"
     if tf.exists():
         try:
@@ -570,6 +605,8 @@ def main() -> int:
     mfma = entry == "shared" or (dt != "f32" and w.group_ratio >= 2 and not args.valu_only)
     kname = "k_decode_mfma" if mfma else "k_decode"
     kernel = kname if not P else f"k_plan + {kname} (partitions) + k_reduce"
+    if args.combined:
+        kernel = f"k_write_plan (new-token write + plan) + {kname} (partitions) + k_reduce"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -598,7 +635,9 @@ def main() -> int:
                                  if args.contiguous else "paged pool"),
                    "step": "pa_cache_write_contiguous + decode"
                    if args.contiguous and not args.through_table
-                   else "pa_cache_write + decode", "parallelism": "none (1 GPU)"},
+                   else ENTRY_NAME[entry_key] + " (write and decode in one call)"
+                   if args.combined else "pa_cache_write + decode",
+                   "parallelism": "none (1 GPU)"},
         "max_abs_err": max_err,
         "tolerance": tol,
         "check": ("output of the last timed step vs the fp64 oracle, all "
@@ -615,7 +654,7 @@ def main() -> int:
                      "traffic": traffic, "kernel": kernel,
                      "avg_launch_us": round(dec_ms * 1e3, 3),
                      "median_launch_us": round(float(np.median(dec_all)) * 1e3, 3),
-                     "algorithmic_bytes_per_launch": dec_bytes,
+                     "algorithmic_bytes_per_launch": timed_bytes,
                      "logical_bytes_per_launch": logical_bytes},
         "cpu_baseline": cpu,
         "read_ceiling": ceiling,

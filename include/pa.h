@@ -176,7 +176,9 @@ size_t pa_decode_splitk_workspace_bytes(int num_seqs, int num_heads, int head_di
  *
  * max_context_len is a host-known bound on every context_lens[s] (no device
  * to host copy is made); it must not exceed max_blocks_per_seq * block_size.
- * A sequence longer than it gets a NaN output row.  `workspace` must hold
+ * It sizes the grid at ceil(max_context_len / partition_size) partitions
+ * per sequence: a sequence that needs more gets a NaN output row (a longer
+ * one that still fits them is computed normally).  `workspace` must hold
  * pa_decode_splitk_workspace_bytes(...) bytes, 16-byte aligned; its contents
  * on entry do not matter and are undefined on exit.
  */
@@ -279,6 +281,45 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
                             int dtype, int num_groups, int max_group_size, int partition_size,
                             int max_context_len, void* workspace, size_t workspace_bytes,
                             int flags, void* stream);
+
+/*
+ * pa_write_decode_splitk, pa_write_decode_shared_prefix -- one decode step
+ * in one call: pa_cache_write of each sequence's new token, then
+ * pa_decode_splitk (resp. pa_decode_shared_prefix) over the updated pools.
+ * The pages store a sequence's K/V block by block through its table and
+ * compute attention over the gathered blocks ("IO-5 vLLM Paged Attention",
+ * sections 2-4); the new token's write is the reading stated at
+ * pa_cache_write (position context_lens[s]-1, which the decode then
+ * attends to).  The pools and `out` end with exactly the bytes the two
+ * separate calls, in that order on one stream, would give.
+ *
+ * Why a combined call: the split-K plan reads only the lengths (and
+ * groups), the write only the lengths, tables and new rows, so the write
+ * runs in the plan's launch -- one launch fewer per step.
+ *
+ * Arguments: those of pa_decode_splitk (resp. pa_decode_shared_prefix),
+ * with k_pool and v_pool written, plus k_new and v_new
+ * ([num_seqs][num_kv_heads][head_dim], 16-byte aligned) as for
+ * pa_cache_write.  k_new and v_new must not overlap the pools, `out` or the
+ * workspace.  Every check of both calls applies; if one fails nothing is
+ * launched.  num_seqs == 0 is a no-op.
+ */
+int pa_write_decode_splitk(void* out, const void* q, void* k_pool, void* v_pool,
+                           const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                           int block_size, int max_blocks_per_seq, int num_blocks,
+                           float scale, int dtype, int partition_size, int max_context_len,
+                           void* workspace, size_t workspace_bytes, int flags, void* stream);
+int pa_write_decode_shared_prefix(void* out, const void* q, void* k_pool, void* v_pool,
+                                  const void* k_new, const void* v_new,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* seq_group, const int32_t* group_prefix_len,
+                                  int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int num_blocks,
+                                  float scale, int dtype, int num_groups, int max_group_size,
+                                  int partition_size, int max_context_len, void* workspace,
+                                  size_t workspace_bytes, int flags, void* stream);
 
 /*
  * pa_decode_contiguous -- the same decode attention over a contiguous KV

@@ -37,6 +37,9 @@ _SIGNATURES = {
     "pa_decode_splitk": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
                          [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
                           _c_void_p]),
+    "pa_write_decode_splitk": (_c_int, [_c_void_p] * 8 + [_c_int] * 7 +
+                               [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
+                                _c_void_p]),
     "pa_decode_splitk_noalloc": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
                                  [_c_float, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
     "pa_cache_write_contiguous": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 + [_c_void_p]),
@@ -70,6 +73,9 @@ _SIGNATURES = {
     "pa_decode_shared_prefix": (_c_int, [_c_void_p] * 8 + [_c_int] * 7 +
                                 [_c_float] + [_c_int] * 5 + [_c_void_p, _c_size_t, _c_int,
                                                               _c_void_p]),
+    "pa_write_decode_shared_prefix": (_c_int, [_c_void_p] * 10 + [_c_int] * 7 +
+                                      [_c_float] + [_c_int] * 5 + [_c_void_p, _c_size_t,
+                                                                    _c_int, _c_void_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -250,6 +256,40 @@ def pa_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
     return out
 
 
+def _new_rows(k_new, v_new, k_pool, B, Hkv, d):
+    _dev(k_new, "k_new", k_pool.dtype)
+    _dev(v_new, "v_new", k_pool.dtype)
+    if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+
+
+def pa_write_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           k_new: torch.Tensor, v_new: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           partition_size: int, max_context_len: int, scale: float,
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, shared_kv: bool = False,
+                           valu_only: bool = False, stream=None) -> torch.Tensor:
+    """One decode step: the new token's write (as pa_cache_write), then
+    pa_decode_splitk, in one call (the write runs in the plan's launch).
+    See pa_write_decode_splitk in include/pa.h."""
+    out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
+                                                           context_lens, scale, out)
+    _new_rows(k_new, v_new, k_pool, B, Hkv, d)
+    need = pa_decode_splitk_workspace_bytes(B, Hq, d, max_context_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pa_write_decode_splitk(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, d, bs,
+        MB, NB, scale, _DTYPES.get(q.dtype, -1), int(partition_size), int(max_context_len),
+        workspace.data_ptr(), ws_bytes, _flags(shared_kv, valu_only), _stream(q.device, stream))
+    _check(st, "pa_write_decode_splitk")
+    return out
+
+
 def pa_decode_splitk_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                              block_tables: torch.Tensor, context_lens: torch.Tensor,
                              partition_size: int, max_context_len: int, scale: float,
@@ -383,6 +423,42 @@ def pa_decode_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch
         int(max_context_len), workspace.data_ptr(), ws_bytes,
         PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
     _check(st, "pa_decode_shared_prefix")
+    return out
+
+
+def pa_write_decode_shared_prefix(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                  k_new: torch.Tensor, v_new: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  seq_group: torch.Tensor, group_prefix_len: torch.Tensor,
+                                  max_group_size: int, partition_size: int,
+                                  max_context_len: int, scale: float,
+                                  out: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None,
+                                  shared_kv: bool = False, stream=None) -> torch.Tensor:
+    """One decode step with shared prompts: the new token's write, then
+    pa_decode_shared_prefix, in one call.  See pa_write_decode_shared_prefix
+    in include/pa.h."""
+    out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
+                                                           context_lens, scale, out)
+    _new_rows(k_new, v_new, k_pool, B, Hkv, d)
+    _dev(seq_group, "seq_group", torch.int32)
+    _dev(group_prefix_len, "group_prefix_len", torch.int32)
+    if seq_group.shape != (B,) or group_prefix_len.dim() != 1:
+        raise ValueError("seq_group must be [num_seqs] and group_prefix_len [num_groups]")
+    G = group_prefix_len.shape[0]
+    need = pa_decode_shared_prefix_workspace_bytes(B, Hq, d, max_context_len, partition_size, G)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load().pa_write_decode_shared_prefix(
+        out.data_ptr(), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), k_new.data_ptr(),
+        v_new.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), seq_group.data_ptr(),
+        group_prefix_len.data_ptr() if G else None, B, Hq, Hkv, d, bs, MB, NB, scale,
+        _DTYPES.get(q.dtype, -1), G, int(max_group_size), int(partition_size),
+        int(max_context_len), workspace.data_ptr(), ws_bytes,
+        PA_FLAG_SHARED_KV if shared_kv else 0, _stream(q.device, stream))
+    _check(st, "pa_write_decode_shared_prefix")
     return out
 
 

@@ -111,6 +111,7 @@ pa::DecodeParams make_params(void* out, const void* q, const void* k_pool, const
   p.group_prefix = nullptr;
   p.num_groups = 0;
   p.max_group_size = 1;
+  p.write = nullptr;
   return p;
 }
 
@@ -250,14 +251,18 @@ size_t pa_decode_shared_prefix_workspace_bytes(int num_seqs, int num_heads, int 
   return (bytes + 255) / 256 * 256;
 }
 
-int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
-                            const int32_t* block_tables, const int32_t* context_lens,
-                            const int32_t* seq_group, const int32_t* group_prefix_len,
-                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                            int block_size, int max_blocks_per_seq, int num_blocks, float scale,
-                            int dtype, int num_groups, int max_group_size, int partition_size,
-                            int max_context_len, void* workspace, size_t workspace_bytes,
-                            int flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int shared_prefix_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* seq_group, const int32_t* group_prefix_len, int num_seqs,
+                       int num_heads, int num_kv_heads, int head_dim, int block_size,
+                       int max_blocks_per_seq, int num_blocks, float scale, int dtype,
+                       int num_groups, int max_group_size, int partition_size,
+                       int max_context_len, void* workspace, size_t workspace_bytes, int flags,
+                       const pa::CacheWriteParams* write, void* stream) {
   int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                         dtype, flags);
@@ -297,7 +302,80 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
   p.group_prefix = group_prefix_len;
   p.num_groups = num_groups;
   p.max_group_size = max_group_size;
+  p.write = write;
   return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+// The new-token write of a combined call: the paged pools and tables of the
+// decode.  Checked here only for what the decode's checks do not cover.
+int new_rows_check(int num_seqs, const void* k_new, const void* v_new) {
+  if (num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new) return pa_fail(PA_ERR_NULL, "k_new and v_new are required");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return pa_fail(PA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  return PA_OK;
+}
+
+pa::CacheWriteParams make_write(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                                int max_blocks_per_seq, int num_blocks, int dtype) {
+  pa::CacheWriteParams w;
+  w.k_pool = k_pool;
+  w.v_pool = v_pool;
+  w.k_new = k_new;
+  w.v_new = v_new;
+  w.block_tables = block_tables;
+  w.context_lens = context_lens;
+  w.num_seqs = num_seqs;
+  w.num_kv_heads = num_kv_heads;
+  w.head_dim = head_dim;
+  w.block_size = block_size;
+  w.max_blocks_per_seq = max_blocks_per_seq;
+  w.num_blocks = num_blocks;
+  w.dtype = dtype;
+  w.max_len = 0;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            const int32_t* seq_group, const int32_t* group_prefix_len,
+                            int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                            int dtype, int num_groups, int max_group_size, int partition_size,
+                            int max_context_len, void* workspace, size_t workspace_bytes,
+                            int flags, void* stream) {
+  return shared_prefix_impl(out, q, k_pool, v_pool, block_tables, context_lens, seq_group,
+                            group_prefix_len, num_seqs, num_heads, num_kv_heads, head_dim,
+                            block_size, max_blocks_per_seq, num_blocks, scale, dtype, num_groups,
+                            max_group_size, partition_size, max_context_len, workspace,
+                            workspace_bytes, flags, nullptr, stream);
+}
+
+int pa_write_decode_shared_prefix(void* out, const void* q, void* k_pool, void* v_pool,
+                                  const void* k_new, const void* v_new,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* seq_group, const int32_t* group_prefix_len,
+                                  int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                  int block_size, int max_blocks_per_seq, int num_blocks,
+                                  float scale, int dtype, int num_groups, int max_group_size,
+                                  int partition_size, int max_context_len, void* workspace,
+                                  size_t workspace_bytes, int flags, void* stream) {
+  const int st = new_rows_check(num_seqs, k_new, v_new);
+  if (st) return st;
+  const pa::CacheWriteParams w =
+      make_write(k_pool, v_pool, k_new, v_new, block_tables, context_lens, num_seqs,
+                 num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  return shared_prefix_impl(out, q, k_pool, v_pool, block_tables, context_lens, seq_group,
+                            group_prefix_len, num_seqs, num_heads, num_kv_heads, head_dim,
+                            block_size, max_blocks_per_seq, num_blocks, scale, dtype, num_groups,
+                            max_group_size, partition_size, max_context_len, workspace,
+                            workspace_bytes, flags, &w, stream);
 }
 
 }  // extern "C"
@@ -330,7 +408,7 @@ int splitk_launch(void* out, const void* q, const void* k_pool, const void* v_po
                   int num_heads, int num_kv_heads, int head_dim, int block_size,
                   int max_blocks_per_seq, int num_blocks, float scale, int dtype,
                   int partition_size, int max_context_len, void* workspace, int flags,
-                  void* stream) {
+                  void* stream, const pa::CacheWriteParams* write = nullptr) {
   pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
                                    num_heads, num_kv_heads, head_dim, block_size,
                                    max_blocks_per_seq, num_blocks, scale, dtype, flags);
@@ -338,6 +416,7 @@ int splitk_launch(void* out, const void* q, const void* k_pool, const void* v_po
   p.partition_size = partition_size;
   p.max_partitions = parts > 0 ? parts : 1;
   p.workspace = static_cast<float*>(workspace);
+  p.write = write;
   return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -365,6 +444,34 @@ int pa_decode_splitk(void* out, const void* q, const void* k_pool, const void* v
   return splitk_launch(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                        dtype, partition_size, max_context_len, workspace, flags, stream);
+}
+
+int pa_write_decode_splitk(void* out, const void* q, void* k_pool, void* v_pool,
+                           const void* k_new, const void* v_new, const int32_t* block_tables,
+                           const int32_t* context_lens, int num_seqs, int num_heads,
+                           int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                           int num_blocks, float scale, int dtype, int partition_size,
+                           int max_context_len, void* workspace, size_t workspace_bytes,
+                           int flags, void* stream) {
+  int st = splitk_checks(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                         num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                         scale, dtype, partition_size, max_context_len, flags);
+  if (st) return st;
+  st = new_rows_check(num_seqs, k_new, v_new);
+  if (st) return st;
+  if (num_seqs == 0) return pa_ok();
+  const size_t need = pa_decode_splitk_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                       max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need)
+    return pa_fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need,
+                workspace_bytes, workspace ? "" : ", NULL");
+  if (!aligned16(workspace)) return pa_fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const pa::CacheWriteParams w =
+      make_write(k_pool, v_pool, k_new, v_new, block_tables, context_lens, num_seqs,
+                 num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  return splitk_launch(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                       num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                       dtype, partition_size, max_context_len, workspace, flags, stream, &w);
 }
 
 int pa_decode_splitk_noalloc(void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -1420,7 +1420,7 @@ __device__ __forceinline__ URec run_record(const URec& r, int i) {
 // member record, and each sequence with several partitions as (sequence,
 // partitions) for the reduce, so the later launches never read the lengths
 // or the groups again.  Lengths, groups and group tables are staged in LDS.
-__global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
+__device__ __forceinline__ void plan_body(const PArgs& pa) {
   __shared__ int hist[257];           // bucket counts, then starts (+ total)
   __shared__ int s_tot[kPlanThreads / 64];
   __shared__ int s_split;             // sequences with more than one partition
@@ -1678,6 +1678,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) {
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const PArgs pa) { plan_body(pa); }
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -1779,8 +1781,7 @@ struct CArgs {
 // One thread per 16-byte chunk of a (sequence, KV head) row; copies K and V
 // into row L-1 of the sequence: through its table, or in its contiguous
 // region.
-__global__ __launch_bounds__(256) void k_cache_write(const CArgs a) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void write_chunk(const CArgs& a, int idx) {
   if (idx >= a.num_seqs * a.num_kv_heads * a.row_chunks) return;
   const int c = idx % a.row_chunks;
   const int sg = idx / a.row_chunks;
@@ -1802,6 +1803,20 @@ __global__ __launch_bounds__(256) void k_cache_write(const CArgs a) {
   const size_t src = (size_t)sg * a.row_bytes + (size_t)c * 16;
   *reinterpret_cast<uint4*>(a.k_pool + dst) = *reinterpret_cast<const uint4*>(a.k_new + src);
   *reinterpret_cast<uint4*>(a.v_pool + dst) = *reinterpret_cast<const uint4*>(a.v_new + src);
+}
+
+__global__ __launch_bounds__(256) void k_cache_write(const CArgs a) {
+  write_chunk(a, blockIdx.x * 256 + threadIdx.x);
+}
+
+// The new token's write and the split-K plan in one launch, for a decode
+// step that does both: workgroup 0 (dispatched first) plans, the others
+// write kPlanThreads chunks each.  Neither reads what the other writes (the
+// plan reads lengths and groups; the write reads lengths, tables and new
+// rows), and the partition launch that follows reads both.
+__global__ __launch_bounds__(kPlanThreads) void k_write_plan(const CArgs c, const PArgs p) {
+  if (blockIdx.x == 0) plan_body(p);
+  else write_chunk(c, (blockIdx.x - 1) * kPlanThreads + threadIdx.x);
 }
 
 struct BArgs {
@@ -1955,6 +1970,36 @@ hipError_t launch1(void (*kernel)(A), dim3 grid, dim3 block, size_t lds, hipStre
                    const A& arg) {
   void* args[] = {const_cast<A*>(&arg)};
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, st);
+}
+
+template <typename A, typename B>
+hipError_t launch2(void (*kernel)(A, B), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                   const A& a, const B& b) {
+  void* args[] = {const_cast<A*>(&a), const_cast<B*>(&b)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, lds, st);
+}
+
+// Kernel arguments of the new-token write; chunks = 16-byte pieces of the
+// new rows (one thread each).  False if the grid would not fit an int.
+bool make_cargs(const CacheWriteParams& p, CArgs& ca, long long& chunks) {
+  const int eb = p.dtype == kF32 ? 4 : 2;
+  ca.k_pool = static_cast<uint8_t*>(p.k_pool);
+  ca.v_pool = static_cast<uint8_t*>(p.v_pool);
+  ca.k_new = static_cast<const uint8_t*>(p.k_new);
+  ca.v_new = static_cast<const uint8_t*>(p.v_new);
+  ca.tables = p.block_tables;
+  ca.lens = p.context_lens;
+  ca.num_seqs = p.num_seqs;
+  ca.num_kv_heads = p.num_kv_heads;
+  ca.row_bytes = p.head_dim * eb;
+  ca.row_chunks = ca.row_bytes / 16;
+  const bool contiguous = p.block_tables == nullptr;
+  ca.bs_log2 = contiguous ? 0 : ilog2(p.block_size);
+  ca.max_blocks = p.max_blocks_per_seq;
+  ca.num_blocks = p.num_blocks;
+  ca.max_len = contiguous ? p.max_len : p.max_blocks_per_seq * p.block_size;
+  chunks = (long long)p.num_seqs * p.num_kv_heads * ca.row_chunks;
+  return chunks <= 0x7fffffffLL - 1024;
 }
 
 constexpr size_t kOneWorkgroupPerCuLds = 81 * 1024;
@@ -2179,7 +2224,19 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     pa_.group_start = shared ? reinterpret_cast<int*>(ws + wl.group_start) : nullptr;
     pa_.group_lp = shared ? reinterpret_cast<int*>(ws + wl.group_lp) : nullptr;
     pa_.max_group_size = p.max_group_size;
-    e = launch1(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, pa_);
+    if (p.write != nullptr) {
+      // The new token's write rides in the plan's launch (workgroups 1..).
+      CArgs ca;
+      long long chunks;
+      if (!make_cargs(*p.write, ca, chunks)) return hipErrorInvalidConfiguration;
+      const int wgs = 1 + (int)((chunks + kPlanThreads - 1) / kPlanThreads);
+      e = launch2(k_write_plan, dim3(wgs), dim3(kPlanThreads), 0, stream, ca, pa_);
+    } else {
+      e = launch1(k_plan, dim3(1), dim3(kPlanThreads), 0, stream, pa_);
+    }
+    if (e != hipSuccess) return e;
+  } else if (p.write != nullptr) {
+    e = launch_cache_write(*p.write, stream);
     if (e != hipSuccess) return e;
   }
   if (mfma) {
@@ -2281,25 +2338,9 @@ hipError_t launch_read_probe(const void* buf, size_t tile_bytes, const int32_t* 
 
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
   if (p.num_seqs == 0) return hipSuccess;
-  const int eb = p.dtype == kF32 ? 4 : 2;
   CArgs ca;
-  ca.k_pool = static_cast<uint8_t*>(p.k_pool);
-  ca.v_pool = static_cast<uint8_t*>(p.v_pool);
-  ca.k_new = static_cast<const uint8_t*>(p.k_new);
-  ca.v_new = static_cast<const uint8_t*>(p.v_new);
-  ca.tables = p.block_tables;
-  ca.lens = p.context_lens;
-  ca.num_seqs = p.num_seqs;
-  ca.num_kv_heads = p.num_kv_heads;
-  ca.row_bytes = p.head_dim * eb;
-  ca.row_chunks = ca.row_bytes / 16;
-  const bool contiguous = p.block_tables == nullptr;
-  ca.bs_log2 = contiguous ? 0 : ilog2(p.block_size);
-  ca.max_blocks = p.max_blocks_per_seq;
-  ca.num_blocks = p.num_blocks;
-  ca.max_len = contiguous ? p.max_len : p.max_blocks_per_seq * p.block_size;
-  const long long total = (long long)p.num_seqs * p.num_kv_heads * ca.row_chunks;
-  if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  long long total;
+  if (!make_cargs(p, ca, total)) return hipErrorInvalidConfiguration;
   const int grid = (int)((total + 255) / 256);
   return launch1(k_cache_write, dim3(grid), dim3(256), 0, stream, ca);
 }

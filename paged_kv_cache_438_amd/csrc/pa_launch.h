@@ -14,6 +14,8 @@ enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr int kFlagSharedKV = 1;
 constexpr int kFlagValuOnly = 2;
 
+struct CacheWriteParams;
+
 struct DecodeParams {
   void* out;
   const void* q;
@@ -40,6 +42,9 @@ struct DecodeParams {
   const int32_t* group_prefix;  // [num_groups] shared prompt tokens of each group
   int num_groups;
   int max_group_size;
+  // The new token's write done in the same call (nullptr: none); with a
+  // split-K workspace it runs in the plan's launch.
+  const CacheWriteParams* write;
 };
 
 struct CacheWriteParams {

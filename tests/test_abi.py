@@ -113,6 +113,40 @@ def test_splitk_workspace_sizing_and_rejects(lib):
     assert call(flags=4, wsb=small) == 2
 
 
+def test_write_decode_rejects(lib):
+    """The combined write + split-K decode applies the checks of both calls,
+    and a zero-sequence batch is a no-op with NULL pointers."""
+    small = pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 100, 256)
+
+    def call(kn=P, vn=P, ws=P, wsb=small, P_=256, B=64, dtype=1, tb=P):
+        return lib.pa_write_decode_splitk(P, P, P, P, kn, vn, tb, P, B, 32, 32, 128, 16, 128,
+                                          9000, 0.088, dtype, P_, 100, ws, wsb, 0, None)
+
+    assert call(kn=0) == 1
+    assert call(vn=0) == 1
+    assert call(kn=P + 8) == 2
+    assert call(vn=P + 4) == 2
+    assert call(tb=0) == 1
+    assert call(ws=0) == 4
+    assert call(wsb=small - 1) == 4
+    assert call(P_=24) == 2
+    assert call(dtype=5) == 3
+    assert call(B=0, kn=0, vn=0, ws=0, wsb=0) == 0
+
+    def shared(kn=P, G=2, mg=4, dtype=1, B=64):
+        need = pa.pa_decode_shared_prefix_workspace_bytes(64, 32, 128, 100, 256, 2)
+        return lib.pa_write_decode_shared_prefix(P, P, P, P, kn, P, P, P, P, P, B, 32, 32, 128,
+                                                 16, 128, 9000, 0.088, dtype, G, mg, 256, 100,
+                                                 P, need, 0, None)
+
+    assert shared(kn=0) == 1
+    assert shared(kn=P + 2) == 2
+    assert shared(dtype=0) == 3                  # fp32: the matrix-core path only
+    assert shared(mg=0) == 2
+    assert shared(G=-1) == 2
+    assert shared(B=0, kn=0, mg=1) == 0
+
+
 def test_contiguous_rejects(lib):
     """pa_decode_contiguous checks its arguments before launching anything."""
     need = pa.pa_decode_splitk_workspace_bytes(4, 8, 128, 1000, 256)
