@@ -45,6 +45,7 @@ DEFAULT_ENTRY = {"llama2_7b": ("single", None), "long_bs512": ("splitk", 512),
                  "tiny": ("single", None)}
 ENTRY_NAME = {"single": "pa_decode", "splitk": "pa_decode_splitk",
               "shared": "pa_decode_shared_prefix", "contiguous": "pa_decode_contiguous",
+              "single_combined": "pa_write_decode",
               "splitk_combined": "pa_write_decode_splitk",
               "shared_combined": "pa_write_decode_shared_prefix"}
 
@@ -340,11 +341,10 @@ def main() -> int:
     ap.add_argument("--valu-only", action="store_true",
                     help="grouped heads on the vector ALUs instead of the matrix cores")
     ap.add_argument("--separate-write", action="store_true",
-                    help="split-K and shared-prompt entries: write the new token with "
-                         "pa_cache_write and time the decode call alone, instead of the "
-                         "default single call (pa_write_decode_splitk or "
-                         "pa_write_decode_shared_prefix) that writes in the plan's launch and "
-                         "is timed as the whole step")
+                    help="paged pool: write the new token with pa_cache_write and time the "
+                         "decode call alone, instead of the default single call "
+                         "(pa_write_decode, pa_write_decode_splitk or "
+                         "pa_write_decode_shared_prefix) timed as the whole step")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the read-probe measurement reported beside the roofline")
     ap.add_argument("--block-ops", action="store_true",
@@ -407,10 +407,11 @@ def main() -> int:
         P = args.partition or (w.partition_size or 1024) if entry != "single" else None
     elif args.partition:
         P = args.partition
-    if args.separate_write and (entry == "single" or args.contiguous):
-        raise SystemExit("--separate-write needs a split-K or shared-prompt entry on a paged pool")
-    # Split entries on a paged pool run the step as one call by default.
-    args.combined = entry != "single" and not args.contiguous and not args.separate_write
+    if args.separate_write and args.contiguous:
+        raise SystemExit("--separate-write needs a paged pool (the contiguous cache's write "
+                         "is always its own call)")
+    # On a paged pool the step is one call by default.
+    args.combined = not args.contiguous and not args.separate_write
     t = time.perf_counter()
     case = make_case(w, seed=args.seed, keep_logical=args.contiguous)
     log(f"bench: generated {w.name} seed={case.seed} in {time.perf_counter() - t:.1f} s; "
@@ -516,7 +517,10 @@ def main() -> int:
 
     # The same step as one call: the write runs in the plan's launch.
     def combined():
-        if entry == "shared":
+        if entry == "single":
+            pa.pa_write_decode(q, kp, vp, kn, vn, tb, ln, scale=scale, out=out, shared_kv=shared,
+                               valu_only=args.valu_only)
+        elif entry == "shared":
             pa.pa_write_decode_shared_prefix(q, kp, vp, kn, vn, tb, ln, seq_group, group_prefix,
                                              max_group, P, maxlen, scale=scale, out=out,
                                              workspace=ws, shared_kv=shared)
@@ -620,7 +624,12 @@ def main() -> int:
     mfma = entry == "shared" or (dt != "f32" and w.group_ratio >= 2 and not args.valu_only)
     kname = "k_decode_mfma" if mfma else "k_decode"
     kernel = kname if not P else f"k_plan + {kname} (partitions) + k_reduce"
-    if args.combined:
+    if args.combined and not P:
+        # the vector kernel with one query head per workgroup (odd group), big pages
+        fused = not mfma and w.group_ratio % 2 == 1 and w.block_size >= 16 and not shared
+        kernel = (f"{kname} (with the new-token write)" if fused
+                  else f"k_cache_write + {kname}")
+    elif args.combined:
         kernel = f"k_write_plan (new-token write + plan) + {kname} (partitions) + k_reduce"
     res = {
         "metric": METRIC,

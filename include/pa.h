@@ -283,9 +283,10 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
                             int flags, void* stream);
 
 /*
- * pa_write_decode_splitk, pa_write_decode_shared_prefix -- one decode step
- * in one call: pa_cache_write of each sequence's new token, then
- * pa_decode_splitk (resp. pa_decode_shared_prefix) over the updated pools.
+ * pa_write_decode, pa_write_decode_splitk, pa_write_decode_shared_prefix --
+ * one decode step in one call: pa_cache_write of each sequence's new token,
+ * then pa_decode (resp. pa_decode_splitk, pa_decode_shared_prefix) over the
+ * updated pools.
  * The pages store a sequence's K/V block by block through its table and
  * compute attention over the gathered blocks ("IO-5 vLLM Paged Attention",
  * sections 2-4); the new token's write is the reading stated at
@@ -293,17 +294,30 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
  * attends to).  The pools and `out` end with exactly the bytes the two
  * separate calls, in that order on one stream, would give.
  *
- * Why a combined call: the split-K plan reads only the lengths (and
- * groups), the write only the lengths, tables and new rows, so the write
- * runs in the plan's launch -- one launch fewer per step.
+ * Why a combined call: one launch fewer per step.  The split-K plan reads
+ * only the lengths (and groups), the write only the lengths, tables and new
+ * rows, so the write runs in the plan's launch.  The single pass has no plan
+ * launch; on the vector-ALU kernel (one query head per workgroup: MHA, or
+ * fp32 with an odd group) over blocks of 16 tokens or more without
+ * PA_FLAG_SHARED_KV, the decode launch itself stores the new rows and reads
+ * row L-1 from k_new / v_new (the same bytes); in every other case
+ * pa_write_decode launches the write and then the decode.
  *
- * Arguments: those of pa_decode_splitk (resp. pa_decode_shared_prefix),
- * with k_pool and v_pool written, plus k_new and v_new
- * ([num_seqs][num_kv_heads][head_dim], 16-byte aligned) as for
+ * Arguments: those of pa_decode (resp. pa_decode_splitk,
+ * pa_decode_shared_prefix), with k_pool and v_pool written, plus k_new and
+ * v_new ([num_seqs][num_kv_heads][head_dim], 16-byte aligned) as for
  * pa_cache_write.  k_new and v_new must not overlap the pools, `out` or the
- * workspace.  Every check of both calls applies; if one fails nothing is
- * launched.  num_seqs == 0 is a no-op.
+ * workspace.  The slot a sequence's new token goes to must not be among the
+ * rows any other sequence of the call attends to (a block that receives a
+ * token belongs to one sequence, as copy-on-write ensures).  Every check of
+ * both calls applies; if one fails nothing is launched.  num_seqs == 0 is a
+ * no-op.
  */
+int pa_write_decode(void* out, const void* q, void* k_pool, void* v_pool, const void* k_new,
+                    const void* v_new, const int32_t* block_tables,
+                    const int32_t* context_lens, int num_seqs, int num_heads,
+                    int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                    int num_blocks, float scale, int dtype, int flags, void* stream);
 int pa_write_decode_splitk(void* out, const void* q, void* k_pool, void* v_pool,
                            const void* k_new, const void* v_new,
                            const int32_t* block_tables, const int32_t* context_lens,

@@ -9,13 +9,13 @@ from ._binding import (PA_BF16, PA_F16, PA_F32, PA_FLAG_SHARED_KV, PA_FLAG_VALU_
                        pa_decode_shared_prefix, pa_decode_shared_prefix_workspace_bytes,
                        pa_decode_contiguous, pa_cache_write_contiguous, pa_copy_blocks, pa_device_memory, pa_read_probe, pa_swap_blocks,
                        pa_decode_splitk, pa_decode_splitk_noalloc, pa_decode_splitk_workspace_bytes,
-                       pa_write_decode_splitk, pa_write_decode_shared_prefix,
+                       pa_write_decode, pa_write_decode_splitk, pa_write_decode_shared_prefix,
                        status_str, LIB_PATH)
 
 __all__ = ["pa_cache_write", "pa_decode", "pa_decode_splitk", "pa_decode_splitk_noalloc",
            "pa_decode_splitk_workspace_bytes", "PA_NOALLOC_SCRATCH_BYTES",
            "pa_decode_shared_prefix", "pa_decode_shared_prefix_workspace_bytes",
-           "pa_decode_contiguous", "pa_cache_write_contiguous", "pa_write_decode_splitk",
+           "pa_decode_contiguous", "pa_cache_write_contiguous", "pa_write_decode", "pa_write_decode_splitk",
            "pa_write_decode_shared_prefix", "pa_check_inputs_host", "PaError", "load", "abi_version", "status_str", "last_error",
            "header_functions", "PA_F32", "PA_F16", "PA_BF16", "PA_FLAG_SHARED_KV", "PA_FLAG_VALU_ONLY",
            "LIB_PATH", "BlockManager", "OutOfBlocks", "pa_copy_blocks", "pa_swap_blocks",

@@ -37,6 +37,8 @@ _SIGNATURES = {
     "pa_decode_splitk": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 +
                          [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
                           _c_void_p]),
+    "pa_write_decode": (_c_int, [_c_void_p] * 8 + [_c_int] * 7 + [_c_float, _c_int, _c_int,
+                                                                _c_void_p]),
     "pa_write_decode_splitk": (_c_int, [_c_void_p] * 8 + [_c_int] * 7 +
                                [_c_float, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_int,
                                 _c_void_p]),
@@ -261,6 +263,25 @@ def _new_rows(k_new, v_new, k_pool, B, Hkv, d):
     _dev(v_new, "v_new", k_pool.dtype)
     if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape:
         raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim]")
+
+
+def pa_write_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                    k_new: torch.Tensor, v_new: torch.Tensor, block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, scale: float,
+                    out: Optional[torch.Tensor] = None, shared_kv: bool = False,
+                    valu_only: bool = False, stream=None) -> torch.Tensor:
+    """One decode step: the new token's write (as pa_cache_write), then
+    pa_decode, in one call.  See pa_write_decode in include/pa.h."""
+    out, (B, Hq, Hkv, d, bs, MB, NB), scale = _decode_args(q, k_pool, v_pool, block_tables,
+                                                           context_lens, scale, out)
+    _new_rows(k_new, v_new, k_pool, B, Hkv, d)
+    st = load().pa_write_decode(out.data_ptr(), q.data_ptr(), k_pool.data_ptr(),
+                                v_pool.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, d,
+                                bs, MB, NB, scale, _DTYPES.get(q.dtype, -1),
+                                _flags(shared_kv, valu_only), _stream(q.device, stream))
+    _check(st, "pa_write_decode")
+    return out
 
 
 def pa_write_decode_splitk(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

@@ -357,6 +357,30 @@ int pa_decode_shared_prefix(void* out, const void* q, const void* k_pool, const 
                             workspace_bytes, flags, nullptr, stream);
 }
 
+int pa_write_decode(void* out, const void* q, void* k_pool, void* v_pool, const void* k_new,
+                    const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int num_blocks, float scale, int dtype, int flags,
+                    void* stream) {
+  int st = check_decode(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, num_heads,
+                        num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                        dtype, flags);
+  if (st) return st;
+  st = new_rows_check(num_seqs, k_new, v_new);
+  if (st) return st;
+  if (num_seqs == 0) return pa_ok();
+  pa::DecodeParams p = make_params(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs,
+                                   num_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, num_blocks, scale, dtype, flags);
+  p.partition_size = (int)(ceil_div64((int64_t)max_blocks_per_seq * block_size, 16) * 16);
+  p.max_partitions = 1;
+  const pa::CacheWriteParams w =
+      make_write(k_pool, v_pool, k_new, v_new, block_tables, context_lens, num_seqs,
+                 num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, dtype);
+  p.write = &w;
+  return finish_launch(pa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
 int pa_write_decode_shared_prefix(void* out, const void* q, void* k_pool, void* v_pool,
                                   const void* k_new, const void* v_new,
                                   const int32_t* block_tables, const int32_t* context_lens,

@@ -256,6 +256,10 @@ struct KArgs {
   const uint8_t* v_pool;
   const int32_t* tables;
   const int32_t* lens;
+  // The new token's rows [B][Hkv][D] when the single-pass launch also writes
+  // them (nullptr otherwise): see k_decode's FUSED.
+  const uint8_t* k_new;
+  const uint8_t* v_new;
   float* ws_acc;        // [B][Hq][max_parts][D]
   float2* ws_ml;        // [B][Hq][max_parts] of (max, sum)
   const int* n_units;   // split-K plan: number of units, then of sequences to merge
@@ -571,8 +575,13 @@ struct BlockIds {
 // a whole sequence (single pass, PLAN false: one unit per workgroup), or a
 // partition of the split-K plan (PLAN true: the workgroup takes units in
 // snake order).  Its W waves take the unit's 16-token steps round-robin.
-template <int DT, int D, int W, int GW, int LAYOUT, bool NT, bool PLAN>
+// FUSED (single pass, blocks of 16 tokens or more): the launch also stores
+// each sequence's new token.  Row L-1 is then read from k_new / v_new, which
+// hold the bytes the store puts in the pool, so no workgroup waits for
+// another's store and the arithmetic is that of a decode after the write.
+template <int DT, int D, int W, int GW, int LAYOUT, bool NT, bool PLAN, bool FUSED = false>
 __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
+  static_assert(!FUSED || (!PLAN && LAYOUT == kBigPages), "fused write: single pass, big pages");
   constexpr bool BIG_BLOCKS = LAYOUT != kSmallPages;
   constexpr bool CONTIG = LAYOUT == kContiguous;
   constexpr int EB = Elem<DT>::bytes;
@@ -624,6 +633,32 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
     const int32_t* trow = CONTIG ? nullptr : a.tables + (size_t)s * a.max_blocks;
     bool bad_block = false;
 
+    // FUSED: this lane's slice of the new token's K and V rows.  The last
+    // wave of the sequence's first head chunk (it has the fewest steps when
+    // they do not divide evenly) loads them now and stores them into the
+    // pool after its steps, so no wave waits for them (the same slot and the
+    // same skips as k_cache_write).
+    const uint8_t* kn_row = nullptr;
+    const uint8_t* vn_row = nullptr;
+    const bool writer = FUSED && ch == 0 && wave == W - 1 && r == 0 && t_end >= 1;
+    uint4 kn_val = make_uint4(0, 0, 0, 0), vn_val = kn_val;
+    size_t kn_off = 0;
+    bool kn_store = false;
+    if constexpr (FUSED) {
+      const size_t nrow = ((size_t)s * a.num_kv_heads + g) * ROWB + c * 16;
+      kn_row = a.k_new + nrow;
+      vn_row = a.v_new + nrow;
+      if (writer) {
+        const int pos = t_end - 1;
+        const int phys = trow[pos >> a.bs_log2];
+        kn_store = (unsigned)phys < (unsigned)a.num_blocks;
+        kn_off = (size_t)(kn_store ? phys : 0) * block_bytes + (size_t)g * tile_bytes +
+                 (size_t)(pos & bs_mask) * ROWB + c * 16;
+        kn_val = *reinterpret_cast<const uint4*>(kn_row);
+        vn_val = *reinterpret_cast<const uint4*>(vn_row);
+      }
+    }
+
     // Iteration k of this wave handles the 16-token step starting at step_t0(k).
     const int nk = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
     auto step_t0 = [&](int k) { return t_begin + ((wave + k * W) << 4); };
@@ -656,12 +691,16 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           const int dt = min(i * RPL + r, t_end - 1 - t0);   // last valid row past the end
-          b.k[i] = ld16<NT>(kb + dt * ROWB);
+          const uint8_t* kp = kb + dt * ROWB;
+          if constexpr (FUSED) kp = t0 + dt == t_end - 1 ? kn_row : kp;   // the new token
+          b.k[i] = ld16<NT>(kp);
         }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           const int dt = min(i * RPL + r, t_end - 1 - t0);
-          b.v[i] = ld16<NT>(vb + dt * ROWB);
+          const uint8_t* vp = vb + dt * ROWB;
+          if constexpr (FUSED) vp = t0 + dt == t_end - 1 ? vn_row : vp;
+          b.v[i] = ld16<NT>(vp);
         }
       } else {
 #pragma unroll
@@ -718,6 +757,13 @@ __global__ __launch_bounds__(W * 64) void k_decode(const KArgs a) {
 #else
     run_pipeline<Buf>(nk, load_step, compute_step);
 #endif
+    if constexpr (FUSED) {
+      // The pools are written only here, by the launch that owns them.
+      if (writer && kn_store) {
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(a.k_pool) + kn_off) = kn_val;
+        *reinterpret_cast<uint4*>(const_cast<uint8_t*>(a.v_pool) + kn_off) = vn_val;
+      }
+    }
 
     // Merge the row groups of this wave.
 #pragma unroll
@@ -2011,6 +2057,14 @@ hipError_t launch_decode_t(const KArgs& ka, int layout, bool nt, int grid, hipSt
   // (measured faster than two on the long-context batch): the unused dynamic
   // LDS below is over half of a CU's 160 KiB, so a second one does not fit.
   const size_t lds = (W == 8 && PLAN) ? kOneWorkgroupPerCuLds : 0;
+  // The new-token write inside a single pass (the host checks the case).
+  if (ka.k_new != nullptr) {
+    if constexpr (!PLAN && GW == 1) {
+      if (layout == kBigPages && nt)
+        return launch1(k_decode<DT, D, W, GW, kBigPages, true, false, true>, gd, bd, lds, st, ka);
+    }
+    return hipErrorInvalidValue;
+  }
   // A contiguous cache holds no shared rows: streaming loads only.
   if (layout == kContiguous)
     return launch1(k_decode<DT, D, W, GW, kContiguous, true, PLAN>, gd, bd, lds, st, ka);
@@ -2133,6 +2187,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   ka.v_pool = static_cast<const uint8_t*>(p.v_pool);
   ka.tables = p.block_tables;
   ka.lens = p.context_lens;
+  ka.k_new = nullptr;
+  ka.v_new = nullptr;
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
   const WsLayout wl = ws_layout(p.num_seqs, p.num_heads, p.head_dim, p.max_partitions,
                                 shared ? p.num_groups : -1);
@@ -2236,8 +2292,16 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     }
     if (e != hipSuccess) return e;
   } else if (p.write != nullptr) {
-    e = launch_cache_write(*p.write, stream);
-    if (e != hipSuccess) return e;
+    // A single pass of the vector kernel over blocks of 16 tokens or more
+    // writes the new token itself (k_decode's FUSED); otherwise the write
+    // is its own launch before the decode.
+    if (!mfma && gw == 1 && layout == kBigPages && nt) {
+      ka.k_new = static_cast<const uint8_t*>(p.write->k_new);
+      ka.v_new = static_cast<const uint8_t*>(p.write->v_new);
+    } else {
+      e = launch_cache_write(*p.write, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   if (mfma) {
     e = p.dtype == kF16 ? dispatch_mfma<kF16>(ka, p.head_dim, layout, nt, (int)grid, stream)

@@ -114,7 +114,7 @@ def test_splitk_workspace_sizing_and_rejects(lib):
 
 
 def test_write_decode_rejects(lib):
-    """The combined write + split-K decode applies the checks of both calls,
+    """The combined write + decode entries apply the checks of both calls,
     and a zero-sequence batch is a no-op with NULL pointers."""
     small = pa.pa_decode_splitk_workspace_bytes(64, 32, 128, 100, 256)
 
@@ -138,6 +138,17 @@ def test_write_decode_rejects(lib):
         return lib.pa_write_decode_shared_prefix(P, P, P, P, kn, P, P, P, P, P, B, 32, 32, 128,
                                                  16, 128, 9000, 0.088, dtype, G, mg, 256, 100,
                                                  P, need, 0, None)
+
+    def single(kn=P, vn=P, B=4, d=128, flags=0, out=P):
+        return lib.pa_write_decode(out, P, P, P, kn, vn, P, P, B, 8, 2, d, 16, 8, 64, 0.088, 1,
+                                   flags, None)
+
+    assert single(kn=0) == 1
+    assert single(vn=P + 8) == 2
+    assert single(d=96) == 3
+    assert single(flags=8) == 2
+    assert single(out=0) == 1
+    assert single(B=0, kn=0, vn=0) == 0
 
     assert shared(kn=0) == 1
     assert shared(kn=P + 2) == 2

@@ -28,7 +28,7 @@ def test_more_than_one_gpu_is_refused():
                                   ("--contiguous", "--through-table", "--workload", "tiny"),
                                   ("--contiguous", "--one-block"),
                                   ("--contiguous", "--workload", "shared_prefix"),
-                                  ("--separate-write",),
+                                  ("--separate-write", "--contiguous"),
                                   ("--separate-write", "--contiguous", "--entry", "splitk")])
 def test_layout_options_that_do_not_combine_are_refused(args):
     """Refused before any input is generated or the GPU is touched."""
@@ -44,7 +44,8 @@ def test_layout_options_that_do_not_combine_are_refused(args):
                                   ("--workload", "tiny", "--contiguous", "--entry", "splitk",
                                    "--partition", "16"),
                                   ("--workload", "tiny", "--entry", "splitk", "--partition", "16",
-                                   "--separate-write")])
+                                   "--separate-write"),
+                                  ("--workload", "tiny", "--separate-write")])
 def test_bench_prints_one_json_line(args):
     r = _bench(*args, "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
     assert r.returncode == 0, r.stderr[-2000:]

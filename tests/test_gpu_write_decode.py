@@ -1,6 +1,6 @@
-"""GPU tests of the combined decode step (pa_write_decode_splitk and
-pa_write_decode_shared_prefix): the new token's K/V write and the split-K
-decode in one call.
+"""GPU tests of the combined decode step (pa_write_decode,
+pa_write_decode_splitk and pa_write_decode_shared_prefix): the new token's
+K/V write and the decode in one call.
 
 The step is defined as pa_cache_write followed by the decode on one stream.
 Every case starts from pools whose new-token slots hold NaN (the state
@@ -14,7 +14,9 @@ before the write) and checks three things:
   Attention", section 4 "Attention computation");
 * the output, bit for bit, against the two separate calls.  The kernels
   that compute it are the same, so any difference is an ordering mistake:
-  a decode that read a slot before its write landed.
+  a decode that read a slot before its write landed, or (single pass on
+  the vector kernel, where the decode takes the new row from k_new) a row
+  taken from the wrong place.
 """
 from __future__ import annotations
 
@@ -50,6 +52,19 @@ def _groups(c):
         seq_group[members] = gi
     prefix = np.full(len(c.shared_groups), c.workload.prompt_len, dtype=np.int32)
     return seq_group, prefix, int(c.shared_groups.shape[1])
+
+
+def _step_single(d, lens=None, valu=False, shared_kv=False):
+    return pa.pa_write_decode(d.q, d.k_pool, d.v_pool, d.k_new, d.v_new, d.tables,
+                              d.lens if lens is None else lens, scale=float(d.c.scale),
+                              valu_only=valu, shared_kv=shared_kv)
+
+
+def _separate_single(d, lens=None, valu=False, shared_kv=False):
+    ln = d.lens if lens is None else lens
+    pa.pa_cache_write(d.k_pool, d.v_pool, d.k_new, d.v_new, d.tables, ln)
+    return pa.pa_decode(d.q, d.k_pool, d.v_pool, d.tables, ln, scale=float(d.c.scale),
+                        valu_only=valu, shared_kv=shared_kv)
 
 
 def _step_splitk(d, P, maxlen, lens=None, valu=False):
@@ -94,6 +109,31 @@ def test_write_decode_splitk_small(w):
             assert host_bits(got).tobytes() == host_bits(sep).tobytes(), what
 
 
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_write_decode_single_small(w):
+    """pa_write_decode: the fused launch for one query head per workgroup on
+    blocks of 16 tokens or more, and the two-launch fallback elsewhere
+    (matrix cores, several heads per workgroup, cached loads, small pages)."""
+    c = make_case(w)
+    ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
+                        c.block_size, c.dtype)
+    grouped = w.num_heads > w.num_kv_heads and w.dtype != "f32"
+    variants = [(False, False), (False, True)] + ([(True, False)] if grouped else [])
+    for valu, shared_kv in variants:
+        what = f"{w.name}/single/valu={valu}/shared_kv={shared_kv}"
+        note(f"write+decode single: {what} seed={c.seed} lens={c.context_lens.tolist()}")
+        a, kp0, vp0 = _poisoned(c)
+        got = _step_single(a, valu=valu, shared_kv=shared_kv)
+        b, _, _ = _poisoned(c)
+        sep = _separate_single(b, valu=valu, shared_kv=shared_kv)
+        torch.cuda.synchronize()
+        ek, ev = _expected_pools(c, kp0, vp0)
+        assert host_bits(a.k_pool).tobytes() == ek.tobytes(), what
+        assert host_bits(a.v_pool).tobytes() == ev.tobytes(), what
+        _check_close(host_f64(got), ref, w.dtype, what)
+        assert host_bits(got).tobytes() == host_bits(sep).tobytes(), what
+
+
 @pytest.mark.parametrize("P", [16, 64, 256])
 def test_write_decode_shared_prefix_small(P):
     c = make_case(small_variant(SHARED_PREFIX))
@@ -119,33 +159,40 @@ def test_write_decode_shared_prefix_small(P):
     assert host_bits(got).tobytes() == host_bits(sep).tobytes()
 
 
-def _edge(name, lens, Hq, Hkv, d, dtype, seed=29):
+def _edge(name, lens, Hq, Hkv, d, dtype, seed=29, bs=16):
     return Workload(name=name, num_seqs=len(lens), num_heads=Hq, num_kv_heads=Hkv, head_dim=d,
-                    block_size=16, dtype=dtype, seed=seed, length_kind="fixed",
-                    lengths=tuple(lens), max_blocks_per_seq=max(1, -(-max(lens) // 16)) + 1)
+                    block_size=bs, dtype=dtype, seed=seed, length_kind="fixed",
+                    lengths=tuple(lens), max_blocks_per_seq=max(1, -(-max(lens) // bs)) + 1)
 
 
 EDGE = [
-    ("mha_f16", (0, 1, 15, 16, 17, 100), 2, 2, 128, "f16"),
-    ("gqa_bf16_g8", (1, 0, 16, 33, 99), 16, 2, 128, "bf16"),
-    ("f32_g2_d64", (3, 31, 32, 0, 77), 4, 2, 64, "f32"),
-    ("one_seq_one_row", (1,), 4, 1, 64, "f16"),
+    ("mha_f16", (0, 1, 15, 16, 17, 100), 2, 2, 128, "f16", 16),
+    ("gqa_bf16_g8", (1, 0, 16, 33, 99), 16, 2, 128, "bf16", 16),
+    ("f32_g2_d64", (3, 31, 32, 0, 77), 4, 2, 64, "f32", 16),
+    ("f32_g3_d128", (5, 0, 48, 49, 130), 3, 1, 128, "f32", 16),
+    ("one_seq_one_row", (1,), 4, 1, 64, "f16", 16),
+    ("mha_bf16_bs64", (1, 63, 64, 65, 200, 0), 3, 3, 64, "bf16", 64),
+    ("mha_f16_bs8", (1, 7, 8, 9, 40), 2, 2, 128, "f16", 8),
+    ("mha_f16_bs1", (1, 2, 5), 2, 2, 64, "f16", 1),
 ]
 
 
 @pytest.mark.parametrize("spec", EDGE, ids=lambda s: s[0])
 def test_write_decode_edge_lengths(spec):
-    name, lens, Hq, Hkv, dd, dtype = spec
-    w = _edge(name, lens, Hq, Hkv, dd, dtype)
+    name, lens, Hq, Hkv, dd, dtype, bs = spec
+    w = _edge(name, lens, Hq, Hkv, dd, dtype, bs=bs)
     c = make_case(w)
     ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
                         c.block_size, c.dtype)
     maxlen = max(lens)
-    for P in (16, 48, 512):
+    for P in (None, 16, 48, 512):
         note(f"write+decode edge: {name} P={P} lens={list(lens)}")
         a, kp0, vp0 = _poisoned(c)
-        got = _step_splitk(a, P, maxlen)
+        got = _step_single(a) if P is None else _step_splitk(a, P, maxlen)
+        b, _, _ = _poisoned(c)
+        sep = _separate_single(b) if P is None else _separate_splitk(b, P, maxlen)
         torch.cuda.synchronize()
+        assert host_bits(got).tobytes() == host_bits(sep).tobytes()
         ek, ev = _expected_pools(c, kp0, vp0)
         assert host_bits(a.k_pool).tobytes() == ek.tobytes()
         assert host_bits(a.v_pool).tobytes() == ev.tobytes()
@@ -184,6 +231,38 @@ def test_write_decode_out_of_contract_lengths():
         assert host_bits(a.v_pool).tobytes() == host_bits(b.v_pool).tobytes()
 
 
+def test_write_decode_single_out_of_contract():
+    """Single pass: a negative length, a length past the table, and a new
+    token whose block id is out of range.  The write skips what
+    pa_cache_write skips, those rows are NaN, the rest are exact, and pools
+    and output bits equal the separate calls'."""
+    for dtype, Hq, Hkv in (("f16", 4, 4), ("bf16", 8, 2)):
+        w = _edge(f"violations_single_{dtype}", (10, 40, 64, 7, 33), Hq, Hkv, 128, dtype)
+        c = make_case(w)
+        ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
+                            c.block_size, c.dtype)
+        lens = c.context_lens.copy().astype(np.int32)
+        lens[2] = -1
+        lens[3] = w.max_blocks_per_seq * w.block_size + 1
+        tb = c.block_tables.copy()
+        tb[4, (33 - 1) // 16] = c.num_blocks + 3           # the new token's block
+        note(f"write+decode single violations: {dtype} lens={lens.tolist()}")
+        a, _, _ = _poisoned(c)
+        a.tables = dev_array(tb)
+        got = _step_single(a, lens=dev_array(lens))
+        b, _, _ = _poisoned(c)
+        b.tables = dev_array(tb)
+        sep = _separate_single(b, lens=dev_array(lens))
+        torch.cuda.synchronize()
+        g = host_f64(got)
+        for s_ in (2, 3, 4):
+            assert np.all(np.isnan(g[s_])), s_
+        _check_close(g[:2], ref[:2], dtype, f"single violations {dtype}")
+        assert host_bits(got).tobytes() == host_bits(sep).tobytes()
+        assert host_bits(a.k_pool).tobytes() == host_bits(b.k_pool).tobytes()
+        assert host_bits(a.v_pool).tobytes() == host_bits(b.v_pool).tobytes()
+
+
 def test_write_decode_no_sequences():
     c = make_case(small_variant(GQA70B))
     d = DevCase(c)
@@ -194,11 +273,16 @@ def test_write_decode_no_sequences():
                                     scale=float(c.scale))
     torch.cuda.synchronize()
     assert out.numel() == 0
+    out = pa.pa_write_decode(d.q[:0], d.k_pool, d.v_pool, kn, kn, d.tables[:0], d.lens[:0],
+                             scale=float(c.scale))
+    torch.cuda.synchronize()
+    assert out.numel() == 0
     assert host_bits(d.k_pool).tobytes() == before
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,P", [("gqa_70b", 8192), ("shared_prefix", 2048)])
+@pytest.mark.parametrize("name,P", [("llama2_7b", None), ("gqa_70b", 8192),
+                                    ("shared_prefix", 2048)])
 def test_write_decode_full_size_bitwise(name, P):
     """The benchmark's split workloads at full size, as bench.py runs them:
     pools equal the generator's populated pools, and every output bit equals
@@ -216,6 +300,8 @@ def test_write_decode_full_size_bitwise(name, P):
         got = pa.pa_write_decode_shared_prefix(a.q, a.k_pool, a.v_pool, a.k_new, a.v_new,
                                                a.tables, a.lens, sg, pl, mg, P, maxlen,
                                                scale=float(c.scale))
+    elif P is None:
+        got = _step_single(a)
     else:
         got = _step_splitk(a, P, maxlen)
     torch.cuda.synchronize()
@@ -228,6 +314,8 @@ def test_write_decode_full_size_bitwise(name, P):
         pa.pa_cache_write(b.k_pool, b.v_pool, b.k_new, b.v_new, b.tables, b.lens)
         sep = pa.pa_decode_shared_prefix(b.q, b.k_pool, b.v_pool, b.tables, b.lens, sg, pl, mg,
                                          P, maxlen, scale=float(c.scale))
+    elif P is None:
+        sep = _separate_single(b)
     else:
         sep = _separate_splitk(b, P, maxlen)
     torch.cuda.synchronize()
