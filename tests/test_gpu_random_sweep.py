@@ -6,8 +6,9 @@ head_dim, KV heads, query heads per KV head (1 to 16, including ones that do
 not divide 16), block size 1 to 256, batch, a length mix with zeros and block
 boundaries, and the entry point (single pass, split-K at one of seven
 partition sizes, the vector-ALU-only flag, sharing-aware decode over random
-prompt groups, or decode over a contiguous cache with a random region
-length).  The case is printed before it runs, so a failure names its draw.
+prompt groups, decode over a contiguous cache with a random region length,
+or a whole step -- the new token's write and the decode in one call).  The
+case is printed before it runs, so a failure names its draw.
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ pytestmark = pytest.mark.gpu
 N_PLAIN = 60
 N_SHARED = 24
 N_CONTIGUOUS = 24
+N_STEP = 24
 
 
 def _plain_case(i):
@@ -145,3 +147,69 @@ def test_random_contiguous_matches_oracle_and_paged(i):
                                       w.num_kv_heads)
     _check(host_f64(got), ref, w.dtype, f"sweep contiguous {i}")
     assert host_bits(got).tobytes() == host_bits(paged).tobytes(), f"sweep contiguous {i}"
+
+
+@pytest.mark.parametrize("i", range(N_STEP))
+def test_random_write_decode_step(i):
+    """A whole step in one call (pa_write_decode, pa_write_decode_splitk or
+    pa_write_decode_shared_prefix) from pools whose new-token slots hold NaN:
+    the pools byte for byte against the oracle's write, the output within the
+    bound of the oracle and bit for bit equal to pa_cache_write followed by
+    the decode call."""
+    shared = i % 2 == 1
+    if shared:
+        w, P = _shared_case(2000 + i)
+        entry = "shared"
+    else:
+        w, entry, P = _plain_case(2000 + i)
+        if i % 4 == 0:
+            # one query head per KV head on blocks of 16 tokens or more: the
+            # single pass then writes inside the decode launch
+            bs = max(16, w.block_size)
+            used = sum(-(-L // bs) for L in w.lengths)
+            w = w.replace(num_heads=w.num_kv_heads, block_size=bs, num_blocks=2 * used + 3,
+                          max_blocks_per_seq=max(1, -(-max(w.lengths) // bs)) + 1)
+            entry = "single" if i % 8 == 0 else entry
+    c = make_case(w)
+    valu = entry.endswith("_valu")
+    kind = entry.split("_")[0]
+    maxlen = int(c.context_lens.max(initial=0))
+    note(f"sweep step {i}: {w.dtype} d={w.head_dim} Hq={w.num_heads} Hkv={w.num_kv_heads} "
+         f"bs={w.block_size} lens={c.context_lens.tolist()} entry={entry} P={P}")
+    kp0, vp0 = c.pools_with_new_slots_poisoned()
+    a = DevCase(c, k_pool=kp0, v_pool=vp0)
+    b = DevCase(c, k_pool=kp0, v_pool=vp0)
+    sc = float(c.scale)
+    if kind == "shared":
+        seq_group = np.full(w.num_seqs, -1, dtype=np.int32)
+        for gi, members in enumerate(c.shared_groups):
+            seq_group[members] = gi
+        sg = dev_array(seq_group)
+        pl = dev_array(np.full(len(c.shared_groups), w.prompt_len, dtype=np.int32))
+        mg = int(c.shared_groups.shape[1])
+        got = pa.pa_write_decode_shared_prefix(a.q, a.k_pool, a.v_pool, a.k_new, a.v_new,
+                                               a.tables, a.lens, sg, pl, mg, P, maxlen, scale=sc)
+        pa.pa_cache_write(b.k_pool, b.v_pool, b.k_new, b.v_new, b.tables, b.lens)
+        sep = pa.pa_decode_shared_prefix(b.q, b.k_pool, b.v_pool, b.tables, b.lens, sg, pl, mg,
+                                         P, maxlen, scale=sc)
+    elif kind == "single":
+        got = pa.pa_write_decode(a.q, a.k_pool, a.v_pool, a.k_new, a.v_new, a.tables, a.lens,
+                                 scale=sc, valu_only=valu)
+        pa.pa_cache_write(b.k_pool, b.v_pool, b.k_new, b.v_new, b.tables, b.lens)
+        sep = pa.pa_decode(b.q, b.k_pool, b.v_pool, b.tables, b.lens, scale=sc, valu_only=valu)
+    else:
+        got = pa.pa_write_decode_splitk(a.q, a.k_pool, a.v_pool, a.k_new, a.v_new, a.tables,
+                                        a.lens, partition_size=P, max_context_len=maxlen,
+                                        scale=sc, valu_only=valu)
+        pa.pa_cache_write(b.k_pool, b.v_pool, b.k_new, b.v_new, b.tables, b.lens)
+        sep = pa.pa_decode_splitk(b.q, b.k_pool, b.v_pool, b.tables, b.lens, partition_size=P,
+                                  max_context_len=maxlen, scale=sc, valu_only=valu)
+    torch.cuda.synchronize()
+    ek, ev = oracle.cache_write(kp0, vp0, c.k_new, c.v_new, c.block_tables, c.context_lens,
+                                c.block_size)
+    assert host_bits(a.k_pool).tobytes() == ek.tobytes(), f"sweep step {i}: K pool"
+    assert host_bits(a.v_pool).tobytes() == ev.tobytes(), f"sweep step {i}: V pool"
+    ref = oracle.decode(c.q, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale,
+                        c.block_size, c.dtype)
+    _check(host_f64(got), ref, w.dtype, f"sweep step {i}")
+    assert host_bits(got).tobytes() == host_bits(sep).tobytes(), f"sweep step {i}: bits"
