@@ -345,6 +345,9 @@ def main() -> int:
                          "decode call alone, instead of the default single call "
                          "(pa_write_decode, pa_write_decode_splitk or "
                          "pa_write_decode_shared_prefix) timed as the whole step")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph after the warm-up and replay it for "
+                         "the timed steps (the step's launches, nothing else)")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the read-probe measurement reported beside the roofline")
     ap.add_argument("--block-ops", action="store_true",
@@ -539,6 +542,20 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        # Capture one step; the timed steps replay it.  The step's calls
+        # allocate nothing and launch kernels only.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        step = graph.replay
     K = args.steps
     # The timed region: K steps back to back, HIP events on the launch
     # stream only at its two ends (an event between launches adds a few
@@ -556,7 +573,8 @@ def main() -> int:
     if args.combined:
         # One call per step: the call's average duration is the span over K.
         dec_ms = span_ms / K
-        timing = f"events around the {K} timed steps, one call each"
+        timing = (f"events around the {K} timed steps, one call each" +
+                  (", replayed from a HIP graph" if args.graph else ""))
     else:
         # Two calls per step: the decode alone, K more launches back to back
         # between two events, right after the timed region.
@@ -650,7 +668,7 @@ def main() -> int:
                    "max_len": longest if args.contiguous else None,
                    "entry": ENTRY_NAME[entry_key],
                    "partition_size": P, "accumulate": "f32", "shared_kv_flag": shared,
-                   "valu_only": bool(args.valu_only),
+                   "valu_only": bool(args.valu_only), "hip_graph": bool(args.graph),
                    "global_batch": w.num_seqs, "kv_tokens": tokens,
                    "kv_layout": ("contiguous cache, regions shuffled, through a table"
                                  if args.shuffled else

@@ -45,7 +45,9 @@ def test_layout_options_that_do_not_combine_are_refused(args):
                                    "--partition", "16"),
                                   ("--workload", "tiny", "--entry", "splitk", "--partition", "16",
                                    "--separate-write"),
-                                  ("--workload", "tiny", "--separate-write")])
+                                  ("--workload", "tiny", "--separate-write"),
+                                  ("--workload", "tiny", "--entry", "splitk", "--partition", "16",
+                                   "--graph")])
 def test_bench_prints_one_json_line(args):
     r = _bench(*args, "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
     assert r.returncode == 0, r.stderr[-2000:]
