@@ -282,7 +282,7 @@ def test_write_decode_no_sequences():
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,P", [("llama2_7b", None), ("gqa_70b", 8192),
-                                    ("shared_prefix", 2048)])
+                                    ("long_bs512", 512), ("shared_prefix", 2048)])
 def test_write_decode_full_size_bitwise(name, P):
     """The benchmark's split workloads at full size, as bench.py runs them:
     pools equal the generator's populated pools, and every output bit equals
